@@ -1,0 +1,252 @@
+/*
+ * pagedkv.h -- C ABI of a paged KV-cache decode-attention library for AMD
+ * MI355X (gfx950).
+ *
+ * What the library implements, from the pages it follows:
+ *
+ *  - Page "生成一个字，为什么要背一整本账", section
+ *    "PagedAttention：把操作系统的老智慧搬进推理引擎": each sequence's KV cache
+ *    is cut into fixed-size blocks (16 tokens by default) that may sit anywhere
+ *    in device memory, mapped by a per-sequence block table; blocks are taken
+ *    on demand; shared prefixes are stored once, reference counted and copied
+ *    on write where sequences diverge.
+ *  - Page "AI 陪读顶会论文（三）：KV Cache 显存占用计算与 PagedAttention 原理拆解",
+ *    section "为什么自回归解码…必须使用 KV Cache": at each decode step only the
+ *    new token's k and v are appended, and its query attends with
+ *    softmax(q K^T / sqrt(d)) V over every cached token, itself included;
+ *    section "PagedAttention 的破局哲学": the logical-to-physical block figure
+ *    and the three innovations (non-contiguous blocks, on-demand allocation,
+ *    copy-on-write for branches).
+ *  - Page "生成一个字…", section "显存账本": grouped-query attention, several
+ *    query heads sharing one KV head; section "再往后：压 KV 的三条路线": FP8
+ *    K/V with per-channel scales, and a sliding attention window.
+ *
+ * Conventions for every call
+ *  - Return value: PKV_OK (0) or a negative pkv_status.  On failure
+ *    pkv_last_error() returns a message for the calling thread.  No C++
+ *    exception crosses this interface.
+ *  - Host calls (block tables) validate every argument first and change no
+ *    state when they fail (strong guarantee).
+ *  - Device calls are asynchronous on the given stream (a hipStream_t; NULL is
+ *    the default stream).  They validate their arguments on the host and
+ *    return PKV_E_HIP if the launch itself fails; errors during execution
+ *    surface at the caller's next synchronisation.
+ *  - The pool object owns host metadata only (tables, lengths, reference
+ *    counts, the free-block queue).  Every device pointer is borrowed: the
+ *    caller allocates it, keeps it alive while the pool uses it and frees it.
+ *  - No internal locking: calls on one pool must be serialised by the caller.
+ *    Device work on one pool must be ordered on one stream:
+ *    kv_pool_copy_blocks, then paged_kv_append, then paged_attention_decode.
+ *
+ * Device memory layout of one pool (both buffers contiguous, caller-owned):
+ *    x = 16 / bytes_per_element   (4 for fp32, 8 for fp16/bf16, 16 for fp8)
+ *    K: [num_layers][num_blocks][num_kv_heads][head_dim / x][block_size][x]
+ *    V: [num_layers][num_blocks][num_kv_heads][head_dim][block_size]
+ *  Token `slot` of a block-table lives in physical block slot / block_size at
+ *  offset slot % block_size.  Each (block, KV head) tile of K and of V is one
+ *  contiguous run of block_size * head_dim elements.  K keeps 16-byte groups
+ *  of channels of consecutive tokens together; V is stored channel-major
+ *  inside the tile.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t pkv_status;
+enum {
+  PKV_OK = 0,
+  PKV_E_INVAL = -1,        /* bad argument, unknown sequence, bad state */
+  PKV_E_OOM = -2,          /* not enough free blocks; nothing was changed */
+  PKV_E_DTYPE = -3,        /* dtype combination not supported */
+  PKV_E_UNSUPPORTED = -4,  /* shape without a kernel (head_dim, block size, group) */
+  PKV_E_HIP = -5,          /* a HIP runtime call failed */
+  PKV_E_INTERNAL = -6      /* unexpected failure (e.g. host allocation) */
+};
+
+/* Element types.  Stored as int32_t in the structs below. */
+enum {
+  PKV_F32 = 0,
+  PKV_F16 = 1,
+  PKV_BF16 = 2,
+  PKV_FP8_E4M3 = 3   /* OCP E4M3: bias 7, max finite 448, NaN = S.1111.111 */
+};
+
+typedef void* pkv_stream;           /* a hipStream_t */
+typedef struct kv_pool kv_pool;     /* opaque */
+
+/* One whole-block copy (copy-on-write): physical block src -> dst. */
+typedef struct {
+  int32_t src;
+  int32_t dst;
+} kv_block_copy;
+
+typedef struct {
+  int32_t num_layers;     /* >= 1 */
+  int32_t num_kv_heads;   /* >= 1 */
+  int32_t head_dim;       /* device kernels: 64 or 128 */
+  int32_t block_size;     /* tokens per block; device kernels: 16, 32, 64, 128 */
+  int32_t num_blocks;     /* physical blocks per layer, >= 1 */
+  int32_t kv_dtype;       /* PKV_F32 / PKV_F16 / PKV_BF16 / PKV_FP8_E4M3 */
+  void* k_cache;          /* device, layout above; may be NULL for a host-only pool */
+  void* v_cache;          /* device, layout above; may be NULL for a host-only pool */
+  /* FP8 only (NULL otherwise): device fp32 [num_layers][num_kv_heads][head_dim].
+   * A stored code c stands for e4m3(c) * scale; appends encode
+   * x * inv_scale, where inv_scale is the caller's fp32 value of 1/scale. */
+  const float* k_scale;
+  const float* v_scale;
+  const float* k_inv_scale;
+  const float* v_inv_scale;
+  /* Host, optional: initial order of the free-block queue, a permutation of
+   * 0..num_blocks-1 (NULL: ascending).  Copied at creation. */
+  const int32_t* free_order;
+} kv_pool_desc;
+
+/* Bytes one of the two device buffers (K or V) of a pool must hold:
+ * num_layers * num_blocks * num_kv_heads * block_size * head_dim * element size. */
+pkv_status kv_pool_cache_bytes(const kv_pool_desc* desc, size_t* bytes_out);
+
+/* Create the host side of a pool.  Validates the descriptor (positive sizes, a
+ * permutation in free_order, scales present iff FP8).  All blocks start free
+ * with reference count 0, queued in free_order.  *out receives the handle. */
+pkv_status kv_pool_create(const kv_pool_desc* desc, kv_pool** out);
+/* Release the host side.  Device buffers are not touched.  NULL is a no-op. */
+void kv_pool_destroy(kv_pool* pool);
+
+pkv_status kv_pool_num_free(const kv_pool* pool, int32_t* out);
+/* Reference count of a physical block (0 = free). */
+pkv_status kv_pool_refcount(const kv_pool* pool, int32_t block, int32_t* out);
+/* The free-block queue, front first: up to cap ids into out (host), the
+ * queue length into *n_out. */
+pkv_status kv_pool_free_list(const kv_pool* pool, int32_t* out, int32_t cap, int32_t* n_out);
+
+/* ---- block tables (host only; page "生成一个字…", section "PagedAttention：…";
+ *      page "AI 陪读顶会论文（三）", section "PagedAttention 的破局哲学") ---- */
+
+/* New empty sequence (length 0, no blocks).  Ids count up from 0 and are
+ * never reused. */
+pkv_status block_table_alloc(kv_pool* pool, int32_t* seq_out);
+
+/* Reserve slots for n_tokens new tokens of seq (token n of a sequence, counted
+ * from 0, goes to slot table[n / block_size] * block_size + n % block_size).
+ *  - A block is taken from the front of the free queue exactly when a token
+ *    with n % block_size == 0 arrives (on-demand allocation).
+ *  - If the first new token falls into a partly filled last block whose
+ *    reference count is > 1, that block is copied on write: a fresh block is
+ *    taken, {old, new} is written to cow_out[0], the old block's count drops
+ *    by one and the table points at the new block.  The caller must run
+ *    kv_pool_copy_blocks on the pairs before appending tokens.
+ * slots_out: host int64 [n_tokens]; cow_out: host, capacity >= 1;
+ * *n_cow_out: 0 or 1.  PKV_E_OOM (state unchanged) if the free queue cannot
+ * supply every block the call needs. */
+pkv_status block_table_append(kv_pool* pool, int32_t seq, int32_t n_tokens,
+                              int64_t* slots_out, kv_block_copy* cow_out,
+                              int32_t* n_cow_out);
+
+/* One new token for each of n distinct sequences, processed in the given
+ * order, all or nothing.  slots_out: host int64 [n]; cow_out: host, capacity
+ * >= n; *n_cow_out receives the number of copies (in processing order). */
+pkv_status block_table_append_batch(kv_pool* pool, const int32_t* seqs, int32_t n,
+                                    int64_t* slots_out, kv_block_copy* cow_out,
+                                    int32_t* n_cow_out);
+
+/* New sequence sharing every block of parent (each block's count + 1). */
+pkv_status block_table_fork(kv_pool* pool, int32_t parent, int32_t* child_out);
+
+/* Drop a sequence: each block's count - 1, in table order; a block reaching 0
+ * goes to the back of the free queue.  The id becomes invalid. */
+pkv_status block_table_free(kv_pool* pool, int32_t seq);
+
+/* Copy a sequence's table (up to cap entries) and report its block count and
+ * token length.  blocks_out may be NULL when cap == 0. */
+pkv_status block_table_get(const kv_pool* pool, int32_t seq, int32_t* blocks_out,
+                           int32_t cap, int32_t* n_blocks_out, int32_t* len_out);
+
+/* Dense export for the decode kernel: tables_out host int32 [n][max_blocks]
+ * (row i = table of seqs[i], padded with -1), lens_out host int32 [n] (token
+ * counts).  PKV_E_INVAL if a table has more than max_blocks entries. */
+pkv_status block_table_export(const kv_pool* pool, const int32_t* seqs, int32_t n,
+                              int32_t max_blocks, int32_t* tables_out, int32_t* lens_out);
+
+/* ---- device work ---- */
+
+/* Whole-block copies for copy-on-write (page "生成一个字…", section
+ * "PagedAttention：…"; page "AI 陪读顶会论文（三）", innovation 3): for each
+ * pair, K and V of block dst in every layer become a byte copy of block src.
+ * d_pairs: device array [n].  Pairs with an id outside [0, num_blocks) are
+ * skipped; a dst must not also be a src in the same call. */
+pkv_status kv_pool_copy_blocks(kv_pool* pool, const kv_block_copy* d_pairs, int32_t n,
+                               pkv_stream stream);
+
+/* Write the new tokens' K and V into their slots of one layer (page
+ * "AI 陪读顶会论文（三）", section "为什么自回归解码…必须使用 KV Cache").
+ * d_k, d_v: device [n_tokens][num_kv_heads][head_dim] of src_dtype.
+ * d_slots: device int64 [n_tokens] from block_table_append; a negative slot
+ * or one >= num_blocks * block_size is skipped.
+ * If src_dtype == the pool dtype the bits are copied.  For an FP8 pool,
+ * src_dtype may be PKV_F32, PKV_F16 or PKV_BF16: each value x is widened to
+ * fp32, multiplied in fp32 by inv_scale[layer][head][channel] and encoded to
+ * E4M3 with round-to-nearest-even; magnitudes >= 448 and infinities saturate
+ * to +-448, NaN becomes 0x7F.  Other combinations return PKV_E_DTYPE. */
+pkv_status paged_kv_append(kv_pool* pool, int32_t layer, const void* d_k, const void* d_v,
+                           int32_t src_dtype, const int64_t* d_slots, int32_t n_tokens,
+                           pkv_stream stream);
+
+typedef struct {
+  int32_t layer;
+  int32_t batch;                /* B >= 0 */
+  int32_t num_q_heads;          /* Hq, a multiple of num_kv_heads, Hq / Hkv <= 16 */
+  int32_t max_blocks_per_seq;   /* row length of block_tables */
+  int32_t sliding_window;       /* 0: off; W > 0: keys L-W .. L-1 only */
+  int32_t num_splits;           /* 0: automatic; 1: single pass, one wavefront per
+                                   (sequence, KV head), no workspace; n >= 2: the
+                                   blocks of all (KV head, sequence) pairs, laid end
+                                   to end, are cut into n equal ranges, one per
+                                   wavefront, and partial results are combined by a
+                                   log-sum-exp merge */
+  const void* q;                /* device [B][Hq][head_dim] */
+  int32_t q_dtype;              /* PKV_F32 for an fp32 pool, PKV_F16 for fp16,
+                                   PKV_BF16 for bf16 and FP8 pools */
+  const int32_t* block_tables;  /* device int32 [B][max_blocks_per_seq] */
+  const int32_t* context_lens;  /* device int32 [B]: tokens including the new one */
+  float scale;                  /* multiplies q.k; 1/sqrt(head_dim) by convention */
+  void* out;                    /* device [B][Hq][head_dim] */
+  int32_t out_dtype;            /* PKV_F32 (recommended), PKV_F16 or PKV_BF16 */
+  void* workspace;              /* device, caller-owned, 256-byte aligned */
+  size_t workspace_bytes;       /* >= paged_attention_workspace_size() */
+} paged_decode_args;
+
+/* Workspace paged_attention_decode needs for these arguments (0 for a single
+ * pass).  For num_splits == 0 this queries the current device. */
+pkv_status paged_attention_workspace_size(const kv_pool* pool, const paged_decode_args* args,
+                                          size_t* bytes_out);
+
+/* Decode attention over the paged cache (page "AI 陪读顶会论文（三）", section
+ * "为什么自回归解码…必须使用 KV Cache", the attention equation; GQA from page
+ * "生成一个字…", section "显存账本"):
+ *   for every sequence b and query head h, with G = Hq / Hkv, KV head
+ *   g = h / G, L = context_lens[b] and lo = max(0, L - W) if a window W is
+ *   set (else 0):
+ *     out[b][h] = sum_{j=lo}^{L-1} softmax_j(scale * q[b][h] . k_j) v_j
+ *   where token j of sequence b is read from physical block
+ *   block_tables[b][j / block_size] at offset j % block_size.
+ * FP8 pools are dequantised as code value * per-channel scale.  L = 0 (or an
+ * empty window) gives zeros.  Table entries outside [0, num_blocks) are read
+ * as empty blocks (their tokens are skipped) and L is clamped to
+ * max_blocks_per_seq * block_size, so no access leaves the buffers. */
+pkv_status paged_attention_decode(const kv_pool* pool, const paged_decode_args* args,
+                                  pkv_stream stream);
+
+/* Message describing the last failure on the calling thread ("" if none). */
+const char* pkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

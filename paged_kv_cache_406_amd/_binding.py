@@ -1,0 +1,275 @@
+"""ctypes binding of include/pagedkv.h -- argument marshalling only.
+
+Every function below has the name of the C entry point it calls.  Pointers
+can be given as integers or as torch tensors (their ``data_ptr()``); streams
+default to torch's current stream on the current device.  A negative status
+raises ``PagedKVError`` (``PagedKVOOM`` for pool exhaustion) with the
+library's message.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
+
+PKV_OK, PKV_E_INVAL, PKV_E_OOM, PKV_E_DTYPE, PKV_E_UNSUPPORTED, PKV_E_HIP, PKV_E_INTERNAL = 0, -1, -2, -3, -4, -5, -6
+PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2, 3
+DTYPE_CODE = {"f32": PKV_F32, "f16": PKV_F16, "bf16": PKV_BF16, "fp8": PKV_FP8_E4M3}
+ELEM_BYTES = {PKV_F32: 4, PKV_F16: 2, PKV_BF16: 2, PKV_FP8_E4M3: 1}
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"pagedkv status {status}: {message}")
+        self.status = status
+
+
+class PagedKVOOM(PagedKVError):
+    pass
+
+
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(
+        f"{_LIB_PATH} is missing: build it with `python paged_kv_cache_406_amd/build.py` "
+        "(or __graft_entry__.build()); there is no fallback implementation")
+_lib = ctypes.CDLL(_LIB_PATH)
+
+c_i32, c_i64, c_size, c_vp, c_float = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+P_i32, P_i64 = ctypes.POINTER(c_i32), ctypes.POINTER(c_i64)
+
+
+class kv_block_copy(ctypes.Structure):
+    _fields_ = [("src", c_i32), ("dst", c_i32)]
+
+
+class kv_pool_desc(ctypes.Structure):
+    _fields_ = [("num_layers", c_i32), ("num_kv_heads", c_i32), ("head_dim", c_i32),
+                ("block_size", c_i32), ("num_blocks", c_i32), ("kv_dtype", c_i32),
+                ("k_cache", c_vp), ("v_cache", c_vp),
+                ("k_scale", c_vp), ("v_scale", c_vp), ("k_inv_scale", c_vp), ("v_inv_scale", c_vp),
+                ("free_order", P_i32)]
+
+
+class paged_decode_args(ctypes.Structure):
+    _fields_ = [("layer", c_i32), ("batch", c_i32), ("num_q_heads", c_i32),
+                ("max_blocks_per_seq", c_i32), ("sliding_window", c_i32), ("num_splits", c_i32),
+                ("q", c_vp), ("q_dtype", c_i32),
+                ("block_tables", c_vp), ("context_lens", c_vp),
+                ("scale", c_float), ("out", c_vp), ("out_dtype", c_i32),
+                ("workspace", c_vp), ("workspace_bytes", c_size)]
+
+
+P_pool = c_vp
+P_copy = ctypes.POINTER(kv_block_copy)
+
+_SIGS = {
+    "kv_pool_cache_bytes": (c_i32, [ctypes.POINTER(kv_pool_desc), ctypes.POINTER(c_size)]),
+    "kv_pool_create": (c_i32, [ctypes.POINTER(kv_pool_desc), ctypes.POINTER(c_vp)]),
+    "kv_pool_destroy": (None, [P_pool]),
+    "kv_pool_num_free": (c_i32, [P_pool, P_i32]),
+    "kv_pool_refcount": (c_i32, [P_pool, c_i32, P_i32]),
+    "kv_pool_free_list": (c_i32, [P_pool, P_i32, c_i32, P_i32]),
+    "block_table_alloc": (c_i32, [P_pool, P_i32]),
+    "block_table_append": (c_i32, [P_pool, c_i32, c_i32, P_i64, P_copy, P_i32]),
+    "block_table_append_batch": (c_i32, [P_pool, P_i32, c_i32, P_i64, P_copy, P_i32]),
+    "block_table_fork": (c_i32, [P_pool, c_i32, P_i32]),
+    "block_table_free": (c_i32, [P_pool, c_i32]),
+    "block_table_get": (c_i32, [P_pool, c_i32, P_i32, c_i32, P_i32, P_i32]),
+    "block_table_export": (c_i32, [P_pool, P_i32, c_i32, c_i32, P_i32, P_i32]),
+    "kv_pool_copy_blocks": (c_i32, [P_pool, c_vp, c_i32, c_vp]),
+    "paged_kv_append": (c_i32, [P_pool, c_i32, c_vp, c_vp, c_i32, c_vp, c_i32, c_vp]),
+    "paged_attention_workspace_size": (c_i32, [P_pool, ctypes.POINTER(paged_decode_args), ctypes.POINTER(c_size)]),
+    "paged_attention_decode": (c_i32, [P_pool, ctypes.POINTER(paged_decode_args), c_vp]),
+    "pkv_last_error": (ctypes.c_char_p, []),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+def pkv_last_error() -> str:
+    return _lib.pkv_last_error().decode()
+
+
+def _check(status):
+    if status != PKV_OK:
+        msg = pkv_last_error()
+        if status == PKV_E_OOM:
+            raise PagedKVOOM(status, msg)
+        raise PagedKVError(status, msg)
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _i32_array(values):
+    arr = np.ascontiguousarray(values, dtype=np.int32)
+    return arr, arr.ctypes.data_as(P_i32)
+
+
+# ---- pool ---------------------------------------------------------------
+def make_desc(num_layers, num_kv_heads, head_dim, block_size, num_blocks, kv_dtype,
+              k_cache=None, v_cache=None, k_scale=None, v_scale=None, k_inv_scale=None,
+              v_inv_scale=None, free_order=None):
+    """Fill a kv_pool_desc; kv_dtype is a PKV_* code or 'f32'/'f16'/'bf16'/'fp8'."""
+    d = kv_pool_desc()
+    d.num_layers, d.num_kv_heads, d.head_dim = num_layers, num_kv_heads, head_dim
+    d.block_size, d.num_blocks = block_size, num_blocks
+    d.kv_dtype = DTYPE_CODE.get(kv_dtype, kv_dtype)
+    d.k_cache, d.v_cache = _ptr(k_cache), _ptr(v_cache)
+    d.k_scale, d.v_scale = _ptr(k_scale), _ptr(v_scale)
+    d.k_inv_scale, d.v_inv_scale = _ptr(k_inv_scale), _ptr(v_inv_scale)
+    keep = None
+    if free_order is not None:
+        keep, d.free_order = _i32_array(free_order)
+    d._keep = keep  # the array must outlive kv_pool_create
+    return d
+
+
+def kv_pool_cache_bytes(desc) -> int:
+    out = c_size()
+    _check(_lib.kv_pool_cache_bytes(ctypes.byref(desc), ctypes.byref(out)))
+    return out.value
+
+
+def kv_pool_create(desc) -> int:
+    h = c_vp()
+    _check(_lib.kv_pool_create(ctypes.byref(desc), ctypes.byref(h)))
+    return h.value
+
+
+def kv_pool_destroy(pool) -> None:
+    _lib.kv_pool_destroy(pool)
+
+
+def kv_pool_num_free(pool) -> int:
+    out = c_i32()
+    _check(_lib.kv_pool_num_free(pool, ctypes.byref(out)))
+    return out.value
+
+
+def kv_pool_refcount(pool, block) -> int:
+    out = c_i32()
+    _check(_lib.kv_pool_refcount(pool, block, ctypes.byref(out)))
+    return out.value
+
+
+def kv_pool_free_list(pool):
+    n = c_i32()
+    _check(_lib.kv_pool_free_list(pool, None, 0, ctypes.byref(n)))
+    arr = np.zeros(max(n.value, 1), dtype=np.int32)
+    _check(_lib.kv_pool_free_list(pool, arr.ctypes.data_as(P_i32), n.value, ctypes.byref(n)))
+    return arr[:n.value].tolist()
+
+
+# ---- block tables ---------------------------------------------------------
+def block_table_alloc(pool) -> int:
+    out = c_i32()
+    _check(_lib.block_table_alloc(pool, ctypes.byref(out)))
+    return out.value
+
+
+def block_table_append(pool, seq, n_tokens):
+    """Returns (slots int64 [n], [(src, dst)] copy-on-write pairs)."""
+    slots = np.zeros(max(n_tokens, 1), dtype=np.int64)
+    cow = (kv_block_copy * 1)()
+    ncow = c_i32()
+    _check(_lib.block_table_append(pool, seq, n_tokens, slots.ctypes.data_as(P_i64), cow,
+                                   ctypes.byref(ncow)))
+    return slots[:n_tokens], [(cow[i].src, cow[i].dst) for i in range(ncow.value)]
+
+
+def block_table_append_batch(pool, seqs, slots_out=None, cow_out=None):
+    """One token for each sequence.  Returns (slots int64 [n], cow pairs int32 [k][2]).
+    Optional preallocated ``slots_out`` (int64 [n]) and ``cow_out`` (int32 [n][2])
+    numpy buffers are filled in place."""
+    seq_arr, seq_p = _i32_array(seqs)
+    n = len(seq_arr)
+    slots = slots_out if slots_out is not None else np.zeros(max(n, 1), dtype=np.int64)
+    cows = cow_out if cow_out is not None else np.zeros((max(n, 1), 2), dtype=np.int32)
+    ncow = c_i32()
+    _check(_lib.block_table_append_batch(pool, seq_p, n, slots.ctypes.data_as(P_i64),
+                                         cows.ctypes.data_as(P_copy), ctypes.byref(ncow)))
+    return slots[:n], cows[:ncow.value]
+
+
+def block_table_fork(pool, parent) -> int:
+    out = c_i32()
+    _check(_lib.block_table_fork(pool, parent, ctypes.byref(out)))
+    return out.value
+
+
+def block_table_free(pool, seq) -> None:
+    _check(_lib.block_table_free(pool, seq))
+
+
+def block_table_get(pool, seq):
+    """Returns (table list, length)."""
+    nb, ln = c_i32(), c_i32()
+    _check(_lib.block_table_get(pool, seq, None, 0, ctypes.byref(nb), ctypes.byref(ln)))
+    arr = np.zeros(max(nb.value, 1), dtype=np.int32)
+    _check(_lib.block_table_get(pool, seq, arr.ctypes.data_as(P_i32), nb.value,
+                                ctypes.byref(nb), ctypes.byref(ln)))
+    return arr[:nb.value].tolist(), ln.value
+
+
+def block_table_export(pool, seqs, max_blocks, tables_out=None, lens_out=None):
+    """Returns (tables int32 [n][max_blocks] padded with -1, lens int32 [n]).
+    Optional numpy output buffers (e.g. views of pinned memory) are filled."""
+    seq_arr, seq_p = _i32_array(seqs)
+    n = len(seq_arr)
+    tables = tables_out if tables_out is not None else np.zeros((n, max_blocks), dtype=np.int32)
+    lens = lens_out if lens_out is not None else np.zeros(n, dtype=np.int32)
+    _check(_lib.block_table_export(pool, seq_p, n, max_blocks, tables.ctypes.data_as(P_i32),
+                                   lens.ctypes.data_as(P_i32)))
+    return tables, lens
+
+
+# ---- device work ------------------------------------------------------------
+def kv_pool_copy_blocks(pool, d_pairs, n, stream=None) -> None:
+    _check(_lib.kv_pool_copy_blocks(pool, _ptr(d_pairs), n, _stream(stream)))
+
+
+def paged_kv_append(pool, layer, d_k, d_v, src_dtype, d_slots, n_tokens, stream=None) -> None:
+    _check(_lib.paged_kv_append(pool, layer, _ptr(d_k), _ptr(d_v), DTYPE_CODE.get(src_dtype, src_dtype),
+                                _ptr(d_slots), n_tokens, _stream(stream)))
+
+
+def make_decode_args(layer, batch, num_q_heads, max_blocks_per_seq, q, q_dtype, block_tables,
+                     context_lens, scale, out, out_dtype="f32", sliding_window=0, num_splits=0,
+                     workspace=None, workspace_bytes=0):
+    a = paged_decode_args()
+    a.layer, a.batch, a.num_q_heads = layer, batch, num_q_heads
+    a.max_blocks_per_seq, a.sliding_window, a.num_splits = max_blocks_per_seq, sliding_window, num_splits
+    a.q, a.q_dtype = _ptr(q), DTYPE_CODE.get(q_dtype, q_dtype)
+    a.block_tables, a.context_lens = _ptr(block_tables), _ptr(context_lens)
+    a.scale = scale
+    a.out, a.out_dtype = _ptr(out), DTYPE_CODE.get(out_dtype, out_dtype)
+    a.workspace, a.workspace_bytes = _ptr(workspace), workspace_bytes
+    return a
+
+
+def paged_attention_workspace_size(pool, args) -> int:
+    out = c_size()
+    _check(_lib.paged_attention_workspace_size(pool, ctypes.byref(args), ctypes.byref(out)))
+    return out.value
+
+
+def paged_attention_decode(pool, args, stream=None) -> None:
+    _check(_lib.paged_attention_decode(pool, ctypes.byref(args), _stream(stream)))

@@ -1,0 +1,326 @@
+// Block tables of a paged KV pool: free-block queue, per-sequence tables,
+// reference counts, on-demand append with copy-on-write, fork and free.
+//
+// Page "生成一个字，为什么要背一整本账", section
+// "PagedAttention：把操作系统的老智慧搬进推理引擎": blocks of a fixed number of
+// tokens, mapped through a per-sequence table, taken on demand, shared
+// prefixes stored once with reference counts and copied on write where
+// sequences diverge.  Page "AI 陪读顶会论文（三）", section
+// "PagedAttention 的破局哲学": tokens 1-16 in logical block 0, 17-32 in
+// block 1, ...; the second block is taken when the 17th token arrives.
+//
+// Policy where the pages are silent: tokens counted from 0; FIFO free queue
+// seeded from free_order; blocks released in table order; lazy copy-on-write
+// of a shared, partly filled last block at the first append into it; every
+// mutating call either fully succeeds or changes nothing.
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <unordered_map>
+
+#include "pool_internal.h"
+
+namespace pkv {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+pkv_status fail(pkv_status code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int elem_bytes(int32_t dtype) {
+  switch (dtype) {
+    case PKV_F32: return 4;
+    case PKV_F16: return 2;
+    case PKV_BF16: return 2;
+    case PKV_FP8_E4M3: return 1;
+    default: return 0;
+  }
+}
+
+static inline int32_t pop_free(kv_pool* p) {
+  int32_t b = p->ring[p->head];
+  p->head = (p->head + 1) % (int64_t)p->ring.size();
+  p->count--;
+  return b;
+}
+
+static inline void push_free(kv_pool* p, int32_t b) {
+  p->ring[(p->head + p->count) % (int64_t)p->ring.size()] = b;
+  p->count++;
+}
+
+// Blocks one append of n tokens to s needs, given an effective reference
+// count of its last block.
+static inline int64_t blocks_needed(const Sequence& s, int64_t n, int32_t bs,
+                                    int32_t last_ref, bool* cow) {
+  const int64_t before = (s.len + bs - 1) / bs;
+  const int64_t after = (s.len + n + bs - 1) / bs;
+  *cow = n > 0 && (s.len % bs) != 0 && last_ref > 1;
+  return (after - before) + (*cow ? 1 : 0);
+}
+
+// Performs an append whose block needs were checked; cannot fail.
+static void do_append(kv_pool* p, Sequence& s, int64_t n, int64_t* slots,
+                      kv_block_copy* cow, int32_t* n_cow) {
+  const int32_t bs = p->desc.block_size;
+  const int64_t start = s.len;
+  for (int64_t pos = start; pos < start + n; ++pos) {
+    if (pos % bs == 0) {
+      int32_t b = pop_free(p);
+      p->refcount[b] = 1;
+      s.table.push_back(b);
+    } else if (pos == start && p->refcount[s.table[pos / bs]] > 1) {
+      int32_t old = s.table[pos / bs];
+      int32_t nw = pop_free(p);
+      p->refcount[old] -= 1;
+      p->refcount[nw] = 1;
+      s.table[pos / bs] = nw;
+      cow[*n_cow].src = old;
+      cow[*n_cow].dst = nw;
+      (*n_cow)++;
+    }
+    slots[pos - start] = (int64_t)s.table[pos / bs] * bs + pos % bs;
+  }
+  s.len = start + n;
+}
+
+}  // namespace pkv
+
+using namespace pkv;
+
+#define PKV_GUARD_BEGIN try {
+#define PKV_GUARD_END                                                   \
+  }                                                                     \
+  catch (const std::bad_alloc&) {                                       \
+    return fail(PKV_E_INTERNAL, "host allocation failed");              \
+  }                                                                     \
+  catch (...) {                                                         \
+    return fail(PKV_E_INTERNAL, "unexpected internal error");           \
+  }
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+pkv_status kv_pool_cache_bytes(const kv_pool_desc* d, size_t* bytes_out) {
+  if (!d || !bytes_out) return fail(PKV_E_INVAL, "null argument");
+  const int eb = elem_bytes(d->kv_dtype);
+  if (!eb) return fail(PKV_E_DTYPE, "unknown kv_dtype");
+  if (d->num_layers <= 0 || d->num_kv_heads <= 0 || d->head_dim <= 0 ||
+      d->block_size <= 0 || d->num_blocks <= 0)
+    return fail(PKV_E_INVAL, "sizes must be positive");
+  *bytes_out = (size_t)d->num_layers * (size_t)d->num_blocks * (size_t)d->num_kv_heads *
+               (size_t)d->block_size * (size_t)d->head_dim * (size_t)eb;
+  return PKV_OK;
+}
+
+pkv_status kv_pool_create(const kv_pool_desc* d, kv_pool** out) {
+  PKV_GUARD_BEGIN
+  if (!d || !out) return fail(PKV_E_INVAL, "null argument");
+  *out = nullptr;
+  size_t bytes = 0;
+  pkv_status st = kv_pool_cache_bytes(d, &bytes);
+  if (st != PKV_OK) return st;
+  const bool fp8 = d->kv_dtype == PKV_FP8_E4M3;
+  const bool any_scale = d->k_scale || d->v_scale || d->k_inv_scale || d->v_inv_scale;
+  const bool all_scale = d->k_scale && d->v_scale && d->k_inv_scale && d->v_inv_scale;
+  if (fp8 && !all_scale) return fail(PKV_E_INVAL, "FP8 pool needs k/v scale and inv_scale");
+  if (!fp8 && any_scale) return fail(PKV_E_INVAL, "scales are only for FP8 pools");
+  if ((d->k_cache == nullptr) != (d->v_cache == nullptr))
+    return fail(PKV_E_INVAL, "k_cache and v_cache must both be set or both be NULL");
+  kv_pool* p = new kv_pool();
+  p->desc = *d;
+  p->desc.free_order = nullptr;
+  const int32_t nb = d->num_blocks;
+  p->ring.resize(nb);
+  p->refcount.assign(nb, 0);
+  if (d->free_order) {
+    std::vector<char> seen(nb, 0);
+    for (int32_t i = 0; i < nb; ++i) {
+      int32_t b = d->free_order[i];
+      if (b < 0 || b >= nb || seen[b]) {
+        delete p;
+        return fail(PKV_E_INVAL, "free_order is not a permutation of 0..num_blocks-1");
+      }
+      seen[b] = 1;
+      p->ring[i] = b;
+    }
+  } else {
+    for (int32_t i = 0; i < nb; ++i) p->ring[i] = i;
+  }
+  p->head = 0;
+  p->count = nb;
+  *out = p;
+  return PKV_OK;
+  PKV_GUARD_END
+}
+
+void kv_pool_destroy(kv_pool* p) { delete p; }
+
+pkv_status kv_pool_num_free(const kv_pool* p, int32_t* out) {
+  if (!p || !out) return fail(PKV_E_INVAL, "null argument");
+  *out = (int32_t)p->count;
+  return PKV_OK;
+}
+
+pkv_status kv_pool_refcount(const kv_pool* p, int32_t block, int32_t* out) {
+  if (!p || !out) return fail(PKV_E_INVAL, "null argument");
+  if (block < 0 || block >= p->desc.num_blocks) return fail(PKV_E_INVAL, "block id out of range");
+  *out = p->refcount[block];
+  return PKV_OK;
+}
+
+pkv_status kv_pool_free_list(const kv_pool* p, int32_t* out, int32_t cap, int32_t* n_out) {
+  if (!p || !n_out || (cap > 0 && !out) || cap < 0) return fail(PKV_E_INVAL, "bad argument");
+  const int64_t n = std::min<int64_t>(cap, p->count);
+  for (int64_t i = 0; i < n; ++i) out[i] = p->ring[(p->head + i) % (int64_t)p->ring.size()];
+  *n_out = (int32_t)p->count;
+  return PKV_OK;
+}
+
+pkv_status block_table_alloc(kv_pool* p, int32_t* seq_out) {
+  PKV_GUARD_BEGIN
+  if (!p || !seq_out) return fail(PKV_E_INVAL, "null argument");
+  if (p->next_id == INT32_MAX) return fail(PKV_E_INVAL, "sequence ids exhausted");
+  const int32_t id = p->next_id;
+  p->seqs.emplace(id, Sequence());
+  p->next_id++;
+  *seq_out = id;
+  return PKV_OK;
+  PKV_GUARD_END
+}
+
+pkv_status block_table_append(kv_pool* p, int32_t seq, int32_t n_tokens, int64_t* slots_out,
+                              kv_block_copy* cow_out, int32_t* n_cow_out) {
+  PKV_GUARD_BEGIN
+  if (!p || !n_cow_out || !cow_out || (n_tokens > 0 && !slots_out))
+    return fail(PKV_E_INVAL, "null argument");
+  if (n_tokens < 0) return fail(PKV_E_INVAL, "n_tokens must be >= 0");
+  auto it = p->seqs.find(seq);
+  if (it == p->seqs.end()) return fail(PKV_E_INVAL, "unknown sequence id");
+  Sequence& s = it->second;
+  if (s.len + n_tokens > (int64_t)INT32_MAX) return fail(PKV_E_INVAL, "sequence too long");
+  const int32_t bs = p->desc.block_size;
+  const int32_t last_ref = (s.len % bs) ? p->refcount[s.table.back()] : 0;
+  bool cow = false;
+  const int64_t need = blocks_needed(s, n_tokens, bs, last_ref, &cow);
+  // the table grows by at most `need` entries: reserve first so that the
+  // mutation below cannot throw
+  s.table.reserve(s.table.size() + need);
+  if (need > p->count) return fail(PKV_E_OOM, "not enough free blocks");
+  *n_cow_out = 0;
+  do_append(p, s, n_tokens, slots_out, cow_out, n_cow_out);
+  return PKV_OK;
+  PKV_GUARD_END
+}
+
+pkv_status block_table_append_batch(kv_pool* p, const int32_t* seqs, int32_t n,
+                                    int64_t* slots_out, kv_block_copy* cow_out,
+                                    int32_t* n_cow_out) {
+  PKV_GUARD_BEGIN
+  if (!p || !n_cow_out || n < 0 || (n > 0 && (!seqs || !slots_out || !cow_out)))
+    return fail(PKV_E_INVAL, "bad argument");
+  const int32_t bs = p->desc.block_size;
+  // dry run: resolve ids, reject duplicates, count blocks with the reference
+  // counts the earlier sequences of the batch leave behind
+  std::vector<Sequence*> ptrs(n);
+  std::unordered_map<int32_t, int32_t> ref_delta;
+  std::unordered_map<int32_t, char> seen;
+  int64_t need = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = p->seqs.find(seqs[i]);
+    if (it == p->seqs.end()) return fail(PKV_E_INVAL, "unknown sequence id in batch");
+    if (!seen.emplace(seqs[i], 1).second) return fail(PKV_E_INVAL, "duplicate sequence in batch");
+    Sequence& s = it->second;
+    if (s.len + 1 > (int64_t)INT32_MAX) return fail(PKV_E_INVAL, "sequence too long");
+    ptrs[i] = &s;
+    int32_t last_ref = 0;
+    if (s.len % bs) {
+      const int32_t last = s.table.back();
+      auto d = ref_delta.find(last);
+      last_ref = p->refcount[last] + (d == ref_delta.end() ? 0 : d->second);
+    }
+    bool cow = false;
+    need += blocks_needed(s, 1, bs, last_ref, &cow);
+    if (cow) ref_delta[s.table.back()] -= 1;
+  }
+  if (need > p->count) return fail(PKV_E_OOM, "not enough free blocks");
+  for (int32_t i = 0; i < n; ++i) ptrs[i]->table.reserve(ptrs[i]->table.size() + 1);
+  *n_cow_out = 0;
+  for (int32_t i = 0; i < n; ++i) do_append(p, *ptrs[i], 1, slots_out + i, cow_out, n_cow_out);
+  return PKV_OK;
+  PKV_GUARD_END
+}
+
+pkv_status block_table_fork(kv_pool* p, int32_t parent, int32_t* child_out) {
+  PKV_GUARD_BEGIN
+  if (!p || !child_out) return fail(PKV_E_INVAL, "null argument");
+  auto it = p->seqs.find(parent);
+  if (it == p->seqs.end()) return fail(PKV_E_INVAL, "unknown sequence id");
+  if (p->next_id == INT32_MAX) return fail(PKV_E_INVAL, "sequence ids exhausted");
+  Sequence child = it->second;  // copy first: may throw, state untouched
+  const int32_t id = p->next_id;
+  auto res = p->seqs.emplace(id, std::move(child));
+  for (int32_t b : res.first->second.table) p->refcount[b] += 1;
+  p->next_id++;
+  *child_out = id;
+  return PKV_OK;
+  PKV_GUARD_END
+}
+
+pkv_status block_table_free(kv_pool* p, int32_t seq) {
+  PKV_GUARD_BEGIN
+  if (!p) return fail(PKV_E_INVAL, "null argument");
+  auto it = p->seqs.find(seq);
+  if (it == p->seqs.end()) return fail(PKV_E_INVAL, "unknown sequence id");
+  for (int32_t b : it->second.table) {
+    p->refcount[b] -= 1;
+    if (p->refcount[b] == 0) push_free(p, b);
+  }
+  p->seqs.erase(it);
+  return PKV_OK;
+  PKV_GUARD_END
+}
+
+pkv_status block_table_get(const kv_pool* p, int32_t seq, int32_t* blocks_out, int32_t cap,
+                           int32_t* n_blocks_out, int32_t* len_out) {
+  if (!p || !n_blocks_out || !len_out || cap < 0 || (cap > 0 && !blocks_out))
+    return fail(PKV_E_INVAL, "bad argument");
+  auto it = p->seqs.find(seq);
+  if (it == p->seqs.end()) return fail(PKV_E_INVAL, "unknown sequence id");
+  const auto& t = it->second.table;
+  const size_t n = std::min<size_t>(cap, t.size());
+  if (n) std::memcpy(blocks_out, t.data(), n * sizeof(int32_t));
+  *n_blocks_out = (int32_t)t.size();
+  *len_out = (int32_t)it->second.len;
+  return PKV_OK;
+}
+
+pkv_status block_table_export(const kv_pool* p, const int32_t* seqs, int32_t n,
+                              int32_t max_blocks, int32_t* tables_out, int32_t* lens_out) {
+  if (!p || n < 0 || max_blocks < 0 ||
+      (n > 0 && (!seqs || !lens_out || (max_blocks > 0 && !tables_out))))
+    return fail(PKV_E_INVAL, "bad argument");
+  std::vector<const Sequence*> ptrs(n);
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = p->seqs.find(seqs[i]);
+    if (it == p->seqs.end()) return fail(PKV_E_INVAL, "unknown sequence id");
+    if ((int64_t)it->second.table.size() > max_blocks)
+      return fail(PKV_E_INVAL, "table longer than max_blocks");
+    ptrs[i] = &it->second;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const auto& t = ptrs[i]->table;
+    int32_t* row = tables_out + (int64_t)i * max_blocks;
+    std::copy(t.begin(), t.end(), row);
+    std::fill(row + t.size(), row + max_blocks, -1);
+    lens_out[i] = (int32_t)ptrs[i]->len;
+  }
+  return PKV_OK;
+}
+
+}  // extern "C"

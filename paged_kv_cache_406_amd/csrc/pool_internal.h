@@ -1,0 +1,38 @@
+// Host-side state of a paged KV pool, shared by the block-table code
+// (pool.cpp) and the device launch code (kernels.hip).
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "pagedkv.h"
+
+namespace pkv {
+
+struct Sequence {
+  std::vector<int32_t> table;  // logical block i -> physical block id
+  int64_t len = 0;             // tokens stored
+};
+
+}  // namespace pkv
+
+struct kv_pool {
+  kv_pool_desc desc;                 // copy; free_order cleared after use
+  // free-block FIFO as a ring buffer over num_blocks entries
+  std::vector<int32_t> ring;
+  int64_t head = 0;
+  int64_t count = 0;
+  std::vector<int32_t> refcount;
+  std::unordered_map<int32_t, pkv::Sequence> seqs;
+  int32_t next_id = 0;
+};
+
+namespace pkv {
+
+void set_error(const std::string& msg);
+pkv_status fail(pkv_status code, const std::string& msg);
+int elem_bytes(int32_t dtype);
+
+}  // namespace pkv

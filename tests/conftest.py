@@ -27,3 +27,13 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    # name the case on stderr before any GPU work starts, so a run that dies
+    # mid-test still says which case it was
+    if "gpu" in request.keywords:
+        sys.stderr.write(f"\n[gpu-case] {request.node.nodeid}\n")
+        sys.stderr.flush()
+    yield

@@ -1,0 +1,115 @@
+"""Builds device-side state through the C ABI from a workload (GPU tests).
+
+Everything here goes through ``paged_kv_cache_406_amd`` (the HIP library);
+inputs come from ``workloads``.  Nothing here imports the oracle.
+"""
+import math
+
+import numpy as np
+import torch
+
+import paged_kv_cache_406_amd as P
+import workloads as wl
+
+TORCH_INT = {np.dtype(np.uint32): np.int32, np.dtype(np.uint16): np.int16, np.dtype(np.uint8): np.uint8}
+
+
+def to_dev(bits: np.ndarray, device="cuda") -> torch.Tensor:
+    """Raw bit patterns -> device tensor holding the same bytes."""
+    a = np.ascontiguousarray(bits)
+    return torch.from_numpy(a.view(TORCH_INT[a.dtype])).to(device)
+
+
+def from_dev(t: torch.Tensor, np_dtype) -> np.ndarray:
+    return t.cpu().numpy().view(np_dtype)
+
+
+def out_to_f64(out: torch.Tensor, out_dtype: str) -> np.ndarray:
+    if out_dtype == "f32":
+        return out.cpu().numpy().astype(np.float64)
+    bits = out.cpu().numpy().view(np.uint16)
+    return wl.bits_as_f32(bits, out_dtype).astype(np.float64)
+
+
+class GpuState:
+    """Pool + sequences of a workload, built by block_table_append and
+    paged_kv_append, and exported tables."""
+
+    def __init__(self, w, d, free_order=None, scales=None, fill_byte=0xFF, seq_range=None,
+                 kv_source=None):
+        self.w, self.d = w, d
+        order = d.free_order if free_order is None else free_order
+        sc = {}
+        if w.kv_dtype == "fp8":
+            k_scale, v_scale, k_inv, v_inv = scales
+            sc = dict(k_scale=k_scale, v_scale=v_scale, k_inv_scale=k_inv, v_inv_scale=v_inv)
+        self.pool = P.TorchKVPool(w.num_layers, w.num_kv_heads, w.head_dim, w.block_size,
+                                  d.num_blocks, w.kv_dtype, free_order=order, **sc)
+        if fill_byte is not None:
+            # unwritten slots hold NaN patterns in every format
+            self.pool.k_cache.fill_(fill_byte)
+            self.pool.v_cache.fill_(fill_byte)
+        self.seqs = []
+        for b, L in enumerate(d.lengths):
+            s = P.block_table_alloc(self.pool.handle)
+            self.seqs.append(s)
+            L = int(L)
+            if L == 0:
+                continue
+            slots, cows = P.block_table_append(self.pool.handle, s, L)
+            assert not cows
+            if kv_source is not None:
+                kb, vb = kv_source(b, L)
+            else:
+                kb, vb = wl.kv_tokens_bits(w, (1, b), L)
+            self.append(0, kb, vb, slots)
+        torch.cuda.synchronize()
+
+    def append(self, layer, kb, vb, slots):
+        k = to_dev(kb)
+        v = to_dev(vb)
+        sl = torch.from_numpy(np.ascontiguousarray(slots, dtype=np.int64)).cuda()
+        P.paged_kv_append(self.pool.handle, layer, k, v, self.w.src_dtype, sl, len(slots))
+
+    def max_blocks(self):
+        return max(1, max(-(-int(L) // self.w.block_size) for L in self.d.lengths))
+
+    def export(self, seqs=None, max_blocks=None):
+        seqs = self.seqs if seqs is None else seqs
+        mb = max_blocks or self.max_blocks()
+        tables, lens = P.block_table_export(self.pool.handle, seqs, mb)
+        return tables, lens
+
+    def decode(self, q_bits, tables, lens, num_splits=0, window=0, out_dtype="f32", scale=None,
+               layer=0):
+        w = self.w
+        B = len(lens)
+        scale = 1.0 / math.sqrt(w.head_dim) if scale is None else scale
+        qd = to_dev(q_bits)
+        td = torch.from_numpy(np.ascontiguousarray(tables, dtype=np.int32)).cuda()
+        ld = torch.from_numpy(np.ascontiguousarray(lens, dtype=np.int32)).cuda()
+        tdt = torch.float32 if out_dtype == "f32" else torch.int16
+        out = torch.full((B, w.num_q_heads, w.head_dim), -7, dtype=tdt, device="cuda")
+        a = P.make_decode_args(layer, B, w.num_q_heads, tables.shape[1], qd, w.q_dtype, td, ld, scale,
+                               out, out_dtype, sliding_window=window, num_splits=num_splits)
+        ws_bytes = P.paged_attention_workspace_size(self.pool.handle, a)
+        ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+        a.workspace, a.workspace_bytes = ws.data_ptr(), ws_bytes
+        P.paged_attention_decode(self.pool.handle, a)
+        torch.cuda.synchronize()
+        return out_to_f64(out, out_dtype)
+
+    def pool_logical(self):
+        """Device pool bytes re-indexed to logical [layers][NB][Hkv][bs][D] bit patterns."""
+        w = self.w
+        eb = wl.ELEM_BYTES[w.kv_dtype]
+        npd = {4: np.uint32, 2: np.uint16, 1: np.uint8}[eb]
+        x = 16 // eb
+        L, NB, H, BS, D = w.num_layers, self.d.num_blocks, w.num_kv_heads, w.block_size, w.head_dim
+        k = from_dev(self.pool.k_cache, npd).reshape(L, NB, H, D // x, BS, x)
+        k = k.transpose(0, 1, 2, 4, 3, 5).reshape(L, NB, H, BS, D)
+        v = from_dev(self.pool.v_cache, npd).reshape(L, NB, H, D, BS).transpose(0, 1, 2, 4, 3)
+        return np.ascontiguousarray(k), np.ascontiguousarray(v)
+
+    def close(self):
+        self.pool.close()

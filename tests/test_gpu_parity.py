@@ -1,0 +1,257 @@
+"""GPU parity: the HIP library against the oracle on the same seeded inputs.
+
+Bars: block tables, slots and pool bytes (copies, FP8 codes) bit-exact;
+decode outputs within 2e-3 max-abs for fp32 / fp16 / bf16 KV and within 3e-2
+for FP8 KV (oracle run on the same codes and scales); invariances bitwise.
+Sizes span several 16-token tiles, ragged last blocks, several wavefront
+ranges per sequence and empty sequences.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_406_amd as P
+import workloads as wl
+from oracle import decode_attention, e4m3_decode_table, e4m3_encode
+from oracle_state import OracleState, fp8_channel_scales
+from gpu_state import GpuState, to_dev, from_dev
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 2e-3, "f16": 2e-3, "bf16": 2e-3, "fp8": 3e-2}
+
+C1 = wl.WORKLOADS["c1"]
+CASES = {
+    "c1": C1,
+    "mha_f16_bs16": wl.scaled(wl.WORKLOADS["c2"], batch=6, num_q_heads=4, num_kv_heads=4,
+                              lengths_args=(1, 300)),
+    "mha_f16_bs32": wl.scaled(wl.WORKLOADS["c2"], batch=5, num_q_heads=2, num_kv_heads=2,
+                              lengths_args=(1, 300), block_size=32),
+    "mha_f16_bs128": wl.scaled(wl.WORKLOADS["c2"], batch=5, num_q_heads=2, num_kv_heads=2,
+                               lengths_args=(1, 600), block_size=128),
+    "gqa8_bf16": wl.scaled(wl.WORKLOADS["c3"], batch=10, num_q_heads=16, num_kv_heads=2,
+                           lengths_args=(60.0, 0.8, 1, 400)),
+    "gqa16_bf16_d64": wl.scaled(wl.WORKLOADS["c3"], batch=5, num_q_heads=16, num_kv_heads=1,
+                                head_dim=64, lengths_args=(60.0, 0.8, 1, 400), block_size=64),
+    "gqa4_bf16_zero_len": wl.scaled(wl.WORKLOADS["c3"], batch=6, num_q_heads=8, num_kv_heads=2,
+                                    lengths_kind="fixed", lengths_args=(0, 1, 16, 17, 0, 95)),
+    "gqa8_fp8": wl.scaled(wl.WORKLOADS["c5_fp8"], batch=3, num_q_heads=16, num_kv_heads=2,
+                          lengths_kind="fixed", lengths_args=(700, 37, 1), pool_blocks=0),
+    "gqa8_fp8_d64_bs32": wl.scaled(wl.WORKLOADS["c5_fp8"], batch=3, num_q_heads=8, num_kv_heads=1,
+                                   head_dim=64, block_size=32, lengths_kind="fixed",
+                                   lengths_args=(300, 33, 64), pool_blocks=0),
+}
+SPLITS = [1, 0, 2, 5, 64]
+_STATES = {}
+
+
+def _state(name):
+    if name not in _STATES:
+        w = CASES[name]
+        d = wl.draw(w)
+        scales = fp8_channel_scales(w, d) if w.kv_dtype == "fp8" else None
+        ost = OracleState(w, d, scales=scales)
+        gst = GpuState(w, d, scales=scales)
+        _STATES[name] = (w, d, ost, gst)
+    return _STATES[name]
+
+
+def _oracle_out(ost, q, tables, lens, window=0, scale=None):
+    w = ost.w
+    scale = 1.0 / math.sqrt(w.head_dim) if scale is None else scale
+    return decode_attention(ost.pool, 0, q, w.q_dtype, tables, lens, scale, window)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_tables_and_pool_bits_exact(name):
+    w, d, ost, gst = _state(name)
+    gt, gl = gst.export()
+    ot, ol = ost.export()
+    assert np.array_equal(gt, ot) and np.array_equal(gl, ol)
+    k, v = gst.pool_logical()
+    written = ost.pool.written
+    for layer in range(w.num_layers):
+        for blk in range(d.num_blocks):
+            for off in np.nonzero(written[layer, blk])[0]:
+                assert np.array_equal(k[layer, blk, :, off], ost.pool.k[layer, blk, :, off]), (blk, off)
+                assert np.array_equal(v[layer, blk, :, off], ost.pool.v[layer, blk, :, off]), (blk, off)
+
+
+@pytest.mark.parametrize("splits", SPLITS)
+@pytest.mark.parametrize("name", list(CASES))
+def test_decode_parity(name, splits):
+    w, d, ost, gst = _state(name)
+    tables, lens = ost.export()
+    q = wl.q_bits(w)
+    ref = _oracle_out(ost, q, tables, lens)
+    got = gst.decode(q, tables, lens, num_splits=splits)
+    assert np.isfinite(got).all()
+    err = np.abs(got - ref).max()
+    assert err <= TOL[w.kv_dtype], (name, splits, err)
+
+
+@pytest.mark.parametrize("window", [1, 5, 16, 40, 10000])
+@pytest.mark.parametrize("name", ["gqa8_bf16", "mha_f16_bs128", "gqa8_fp8", "c1"])
+def test_sliding_window_parity(name, window):
+    w, d, ost, gst = _state(name)
+    tables, lens = ost.export()
+    q = wl.q_bits(w)
+    ref = _oracle_out(ost, q, tables, lens, window=window)
+    for splits in (1, 0, 3):
+        got = gst.decode(q, tables, lens, num_splits=splits, window=window)
+        err = np.abs(got - ref).max()
+        assert err <= TOL[w.kv_dtype], (name, window, splits, err)
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
+def test_low_precision_outputs(out_dtype):
+    w, d, ost, gst = _state("gqa8_bf16")
+    tables, lens = ost.export()
+    q = wl.q_bits(w)
+    ref = _oracle_out(ost, q, tables, lens)
+    got = gst.decode(q, tables, lens, num_splits=0, out_dtype=out_dtype)
+    ulp = 2.0 ** -8 if out_dtype == "bf16" else 2.0 ** -11
+    assert (np.abs(got - ref) <= 2e-3 + np.abs(ref) * ulp).all()
+
+
+def test_split_results_agree_and_are_deterministic():
+    w, d, ost, gst = _state("gqa8_bf16")
+    tables, lens = ost.export()
+    q = wl.q_bits(w)
+    runs = {s: gst.decode(q, tables, lens, num_splits=s) for s in (1, 0, 7)}
+    for s in (1, 0, 7):
+        again = gst.decode(q, tables, lens, num_splits=s)
+        assert np.array_equal(again, runs[s])          # run to run, bitwise
+    assert np.abs(runs[1] - runs[0]).max() < 1e-4
+    assert np.abs(runs[1] - runs[7]).max() < 1e-4
+
+
+@pytest.mark.parametrize("splits", [1, 0, 3])
+def test_placement_permutation_bitwise(splits):
+    w = CASES["gqa8_bf16"]
+    d = wl.draw(w)
+    q = wl.q_bits(w)
+    outs = []
+    for seed in (1, 2):
+        order = np.random.default_rng(seed).permutation(d.num_blocks).astype(np.int32)
+        gst = GpuState(w, d, free_order=order)
+        tables, lens = gst.export()
+        outs.append(gst.decode(q, tables, lens, num_splits=splits))
+        gst.close()
+    assert np.array_equal(outs[0], outs[1])
+
+
+def test_fork_cow_identity():
+    w = wl.scaled(wl.WORKLOADS["c4"], batch=3, num_q_heads=8, num_kv_heads=2, lengths_kind="fixed",
+                  lengths_args=(40, 77, 16), pool_blocks=40)
+    d = wl.draw(w)
+    ost = OracleState(w, d)
+    gst = GpuState(w, d)
+    h = gst.pool.handle
+    # fork every sequence, then append the same token to child and parent
+    kids = [P.block_table_fork(h, s) for s in gst.seqs]
+    okids = [ost.bm.fork(s) for s in ost.seqs]
+    order = []
+    for s, k in zip(gst.seqs, kids):
+        order += [k, s]
+    oorder = []
+    for s, k in zip(ost.seqs, okids):
+        oorder += [k, s]
+    kb, vb, _ = wl.step_tokens_bits(w, 0, batch=3)
+    kb2, vb2 = np.repeat(kb, 2, axis=0), np.repeat(vb, 2, axis=0)
+    slots, cows = P.block_table_append_batch(h, order)
+    oslots, ocows = ost.bm.append_batch(oorder)
+    assert slots.tolist() == oslots and [tuple(c) for c in cows.tolist()] == ocows
+    assert len(ocows) == 2          # lengths 40 and 77 end inside a block; 16 does not
+    pairs = torch.from_numpy(np.ascontiguousarray(cows, dtype=np.int32)).cuda()
+    P.kv_pool_copy_blocks(h, pairs, len(cows))
+    gst.append(0, kb2, vb2, slots)
+    ost.pool.copy_blocks(ocows)
+    ost.pool.append(0, kb2, vb2, w.src_dtype, oslots)
+    torch.cuda.synchronize()
+    # pool bytes bit-exact after copy-on-write
+    k, v = gst.pool_logical()
+    for blk in range(d.num_blocks):
+        for off in np.nonzero(ost.pool.written[0, blk])[0]:
+            assert np.array_equal(k[0, blk, :, off], ost.pool.k[0, blk, :, off])
+            assert np.array_equal(v[0, blk, :, off], ost.pool.v[0, blk, :, off])
+    # each child decodes bitwise equal to its parent
+    q = wl.q_bits(w)
+    q2 = np.repeat(q, 2, axis=0)
+    tables, lens = P.block_table_export(h, order, 8)
+    out = gst.decode(q2, tables, lens)
+    for i in range(3):
+        assert np.array_equal(out[2 * i], out[2 * i + 1])
+    ot, ol = ost.bm.export(oorder, 8)
+    ref = _oracle_out(ost, q2, ot, ol)
+    assert np.abs(out - ref).max() <= 2e-3
+    gst.close()
+
+
+def test_fp8_codes_decode_exactly():
+    # every finite E4M3 value, appended from fp32 with scale 1, read back by
+    # decode of a one-token sequence (softmax weight exactly 1)
+    table = e4m3_decode_table()
+    finite = [c for c in range(256) if c not in (0x7F, 0xFF)]
+    D = 128
+    ntok = -(-len(finite) // D)
+    vals = np.zeros((ntok, 1, D), np.float32)
+    flat = np.array([table[c] for c in finite], np.float32)
+    vals.reshape(-1)[:len(flat)] = flat
+    one = np.ones((1, 1, D), np.float32)
+    pool = P.TorchKVPool(1, 1, D, 16, 4, "fp8", k_scale=one, v_scale=one)
+    h = pool.handle
+    seqs = []
+    for t in range(ntok):
+        s = P.block_table_alloc(h)
+        slots, _ = P.block_table_append(h, s, 1)
+        kd = torch.from_numpy(vals[t:t + 1]).cuda()
+        P.paged_kv_append(h, 0, kd, kd, "f32", torch.from_numpy(slots).cuda(), 1)
+        seqs.append(s)
+    tables, lens = P.block_table_export(h, seqs, 1)
+    q = torch.zeros((ntok, 1, D), dtype=torch.int16, device="cuda")
+    out = torch.zeros((ntok, 1, D), dtype=torch.float32, device="cuda")
+    a = P.make_decode_args(0, ntok, 1, 1, q, "bf16", torch.from_numpy(tables).cuda(),
+                           torch.from_numpy(lens).cuda(), 0.1, out, num_splits=1)
+    P.paged_attention_decode(h, a)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().reshape(-1)[:len(flat)]
+    assert np.array_equal(got, flat)
+    codes = from_dev(pool.v_cache, np.uint8).reshape(4, 1, D, 16)
+    pool.close()
+
+
+def test_fp8_encoder_bit_exact():
+    rng = np.random.default_rng(5)
+    D, n = 128, 64
+    x = np.concatenate([
+        rng.standard_normal(n * D // 2).astype(np.float32) * 50,
+        rng.standard_normal(n * D // 4).astype(np.float32) * 1e-3,
+        rng.uniform(-600, 600, n * D // 4).astype(np.float32)]).reshape(n, 1, D)
+    # exact midpoints and specials in the first rows
+    specials = np.array([1.0625, 1.1875, -1.0625, 2.0 ** -10, 3 * 2.0 ** -10, 448, 460, 464, 1e30,
+                         np.inf, -np.inf, np.nan, -0.0, 0.0, 2.0 ** -7 * 1.0625, 240.0, 232.0],
+                        np.float32)
+    x.reshape(-1)[:len(specials)] = specials
+    scale = np.full((1, 1, D), 1.0, np.float32)
+    inv = scale.copy()
+    inv[0, 0, 1::2] = 0.5           # odd channels scaled by 1/2 before encoding
+    pool = P.TorchKVPool(1, 1, D, 16, 8, "fp8", k_scale=scale, v_scale=scale,
+                         k_inv_scale=inv, v_inv_scale=inv)
+    h = pool.handle
+    s = P.block_table_alloc(h)
+    slots, _ = P.block_table_append(h, s, n)
+    xd = torch.from_numpy(x).cuda()
+    P.paged_kv_append(h, 0, xd, xd, "f32", torch.from_numpy(slots).cuda(), n)
+    torch.cuda.synchronize()
+    want = e4m3_encode((x * inv[0]).astype(np.float32))     # [n][1][D]
+    k = from_dev(pool.k_cache, np.uint8).reshape(8, 1, D // 16, 16, 16).transpose(0, 1, 3, 2, 4).reshape(8, 1, 16, D)
+    v = from_dev(pool.v_cache, np.uint8).reshape(8, 1, D, 16).transpose(0, 1, 3, 2)
+    table, _ = P.block_table_get(h, s)
+    for t in range(n):
+        blk, off = table[t // 16], t % 16
+        assert np.array_equal(k[blk, 0, off], want[t, 0]), t
+        assert np.array_equal(v[blk, 0, off], want[t, 0]), t
+    pool.close()
