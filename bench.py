@@ -1,0 +1,341 @@
+"""Paged decode-attention benchmark on one MI355X.
+
+One step is one pass of the whole decode hot path over one batch:
+  1. host: reserve one slot per sequence (block_table_append_batch: on-demand
+     blocks, copy-on-write of shared partial blocks),
+  2. one host->device copy of the step's metadata (slots, copy pairs, block
+     tables, context lengths) from pinned memory,
+  3. kv_pool_copy_blocks for the copy-on-write pairs,
+  4. paged_kv_append of the new token's K/V,
+  5. paged_attention_decode (range-split decode + log-sum-exp merge).
+Inputs (the cache and every step's q, k, v) are resident in HBM before the
+timed region starts.  Several independently placed copies of the cache are
+rotated so the working set is several times the 256 MB Infinity Cache.
+
+Prints one JSON line.  ``value`` is KV GB/s over the whole step (algorithmic
+bytes of the decode / step time); ``roofline`` is the decode call alone,
+timed with events on the launch stream; ``cpu_baseline`` is the CPU oracle
+timed on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload c3]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+
+METRIC = "paged decode attention: KV GB/s achieved and % of HBM peak; seq·heads/s"
+HBM_PEAK_GBS = 8000.0
+WORKLOAD_NAMES = {
+    "c2": "llama2-7b-mha-decode-layer (B=64, 32/32 heads, d=128, fp16 KV, block 16)",
+    "c2_bs32": "llama2-7b-mha-decode-layer (B=64, 32/32 heads, d=128, fp16 KV, block 32)",
+    "c2_bs128": "llama2-7b-mha-decode-layer (B=64, 32/32 heads, d=128, fp16 KV, block 128)",
+    "c3": "llama2-70b-gqa-decode-layer (B=128, 64/8 heads, d=128, bf16 KV, block 16, lognormal lengths)",
+    "c5": "long-context-128k-decode (B=4, L=131072, 64/8 heads, d=128, bf16 KV, block 16)",
+    "c5_fp8": "long-context-128k-decode-fp8 (B=4, L=131072, 64/8 heads, d=128, FP8-E4M3 KV, block 16)",
+    "c5w": "long-context-128k-window-4096 (B=4, L=131072, 64/8 heads, d=128, bf16 KV, block 16)",
+}
+
+
+def log(msg):
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+def decode_bytes(w, lengths):
+    """Algorithmic bytes of one decode call: KV of every attended token, q,
+    the fp32 output, the block-table entries read, the context lengths and
+    (FP8) the per-channel scales."""
+    eb = wl.ELEM_BYTES[w.kv_dtype]
+    qb = wl.ELEM_BYTES[w.q_dtype]
+    bs = w.block_size
+    kv = tables = 0
+    for L in lengths:
+        L = int(L)
+        lo = max(0, L - w.window) if w.window else 0
+        kv += (L - lo) * w.num_kv_heads * 2 * w.head_dim * eb
+        tables += (-(-L // bs) - lo // bs) * 4 if L > lo else 0
+    B = len(lengths)
+    total = kv + B * w.num_q_heads * w.head_dim * (qb + 4) + tables + B * 4
+    if w.kv_dtype == "fp8":
+        total += 2 * w.num_kv_heads * w.head_dim * 4
+    return total, kv
+
+
+class Replica:
+    """One independently placed copy of the workload's cache."""
+
+    def __init__(self, P, torch, w, d, order, kv_cache, max_blocks, scales):
+        self.P, self.torch, self.w = P, torch, w
+        self.pool = P.TorchKVPool(w.num_layers, w.num_kv_heads, w.head_dim, w.block_size,
+                                  d.num_blocks, w.kv_dtype, free_order=order, **scales)
+        h = self.pool.handle
+        self.seqs = []
+        for b, L in enumerate(d.lengths):
+            s = P.block_table_alloc(h)
+            slots, _ = P.block_table_append(h, s, int(L))
+            kd, vd = kv_cache[b]
+            P.paged_kv_append(h, 0, kd, vd, w.src_dtype, torch.from_numpy(slots).cuda(), int(L))
+            self.seqs.append(s)
+        self.seq_arr = np.asarray(self.seqs, dtype=np.int32)
+        B = len(self.seqs)
+        self.max_blocks = max_blocks
+        # device metadata block: slots (int64 [B]), copy pairs (int32 [B][2]),
+        # tables (int32 [B][max_blocks]), lens (int32 [B])
+        self.n_meta = 2 * B + 2 * B + B * max_blocks + B
+        self.meta = torch.empty(self.n_meta, dtype=torch.int32, device="cuda")
+        self.d_slots = self.meta[: 2 * B].view(torch.int64)
+        self.d_cows = self.meta[2 * B: 4 * B]
+        self.d_tables = self.meta[4 * B: 4 * B + B * max_blocks]
+        self.d_lens = self.meta[4 * B + B * max_blocks:]
+        self.lengths = np.array([int(x) for x in d.lengths], dtype=np.int64)
+
+
+def build_state(args, P, torch):
+    w = wl.WORKLOADS[args.workload]
+    steps_total = args.steps + args.warmup
+    # headroom: every sequence may take one new block per block_size steps
+    extra = w.batch * (-(-steps_total // w.block_size) + 1)
+    d = wl.draw(w, extra_blocks=extra)
+    bytes0, kv0 = decode_bytes(w, d.lengths)
+    reps = args.replicas or max(1, math.ceil(2 * 2 ** 30 / kv0))
+    log(f"workload {w.name}: B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} D={w.head_dim} "
+        f"bs={w.block_size} kv={w.kv_dtype} pool={d.num_blocks} blocks, KV bytes/call={kv0/1e9:.3f} GB, "
+        f"replicas={reps}")
+    t0 = time.time()
+    kv_cache = []
+    absmax_k = np.zeros((w.num_kv_heads, w.head_dim), np.float32)
+    absmax_v = np.zeros((w.num_kv_heads, w.head_dim), np.float32)
+    for b, L in enumerate(d.lengths):
+        kb, vb = wl.kv_tokens_bits(w, (1, b), int(L))
+        if w.kv_dtype == "fp8":
+            absmax_k = np.maximum(absmax_k, np.abs(wl.bits_as_f32(kb, w.src_dtype)).max(axis=0))
+            absmax_v = np.maximum(absmax_v, np.abs(wl.bits_as_f32(vb, w.src_dtype)).max(axis=0))
+        tdt = np.int16 if kb.dtype == np.uint16 else np.int32
+        kv_cache.append((torch.from_numpy(kb.view(tdt)).cuda(), torch.from_numpy(vb.view(tdt)).cuda()))
+    scales = {}
+    if w.kv_dtype == "fp8":
+        ks, _ = wl.fp8_scales(absmax_k)
+        vs, _ = wl.fp8_scales(absmax_v)
+        scales = dict(k_scale=ks[None], v_scale=vs[None])
+    log(f"generated K/V in {time.time() - t0:.1f}s")
+    max_len = int(max(d.lengths)) + steps_total + 1
+    max_blocks = -(-max_len // w.block_size) + 1
+    reps_list = []
+    for r in range(reps):
+        order = np.random.default_rng([w.seed, 5, r]).permutation(d.num_blocks).astype(np.int32)
+        reps_list.append(Replica(P, torch, w, d, order, kv_cache, max_blocks, scales))
+    torch.cuda.synchronize()
+    del kv_cache
+    log(f"built {reps} replicas in {time.time() - t0:.1f}s")
+    # per-step new tokens and queries, resident on the device
+    steps = []
+    for t in range(steps_total):
+        kb, vb, qb = wl.step_tokens_bits(w, t)
+        tdt = np.int16 if kb.dtype == np.uint16 else np.int32
+        qdt = np.int16 if qb.dtype == np.uint16 else np.int32
+        steps.append((torch.from_numpy(kb.view(tdt)).cuda(), torch.from_numpy(vb.view(tdt)).cuda(),
+                      torch.from_numpy(qb.view(qdt)).cuda()))
+    return w, d, reps_list, steps
+
+
+def run(args):
+    import torch
+    import paged_kv_cache_406_amd as P
+
+    torch.cuda.set_device(0)
+    w, d, reps, steps = build_state(args, P, torch)
+    B = w.batch
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    out = torch.empty((B, w.num_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(w.head_dim)
+    args0 = P.make_decode_args(0, B, w.num_q_heads, reps[0].max_blocks, steps[0][2], w.q_dtype,
+                               reps[0].d_tables, reps[0].d_lens, scale, out, "f32",
+                               sliding_window=w.window, num_splits=args.splits)
+    ws_bytes = P.paged_attention_workspace_size(reps[0].pool.handle, args0)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    # pinned staging ring for the per-step metadata
+    ring = []
+    for _ in range(4):
+        buf = torch.empty(reps[0].n_meta, dtype=torch.int32, pin_memory=True)
+        ring.append((buf, buf.numpy(), torch.cuda.Event()))
+    mb = reps[0].max_blocks
+    dev_ev = []
+
+    def step(t, record):
+        rep = reps[t % len(reps)]
+        h = rep.pool.handle
+        buf, npb, ev = ring[t % len(ring)]
+        ev.synchronize()                       # the copy that last used this buffer is done
+        slots_np = npb[: 2 * B].view(np.int64)
+        cows_np = npb[2 * B: 4 * B].reshape(B, 2)
+        tables_np = npb[4 * B: 4 * B + B * mb].reshape(B, mb)
+        lens_np = npb[4 * B + B * mb:]
+        _, cows = P.block_table_append_batch(h, rep.seq_arr, slots_out=slots_np, cow_out=cows_np)
+        P.block_table_export(h, rep.seq_arr, mb, tables_out=tables_np, lens_out=lens_np)
+        rep.lengths += 1
+        rep.meta.copy_(buf, non_blocking=True)
+        ev.record(stream)
+        if len(cows):
+            P.kv_pool_copy_blocks(h, rep.d_cows, len(cows), sptr)
+        kd, vd, qd = steps[t]
+        P.paged_kv_append(h, 0, kd, vd, w.src_dtype, rep.d_slots, B, sptr)
+        a = P.make_decode_args(0, B, w.num_q_heads, mb, qd, w.q_dtype, rep.d_tables, rep.d_lens,
+                               scale, out, "f32", sliding_window=w.window, num_splits=args.splits,
+                               workspace=ws, workspace_bytes=ws_bytes)
+        if record:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            P.paged_attention_decode(h, a, sptr)
+            e1.record(stream)
+            dev_ev.append((e0, e1, rep.lengths.copy()))
+        else:
+            P.paged_attention_decode(h, a, sptr)
+
+    log(f"warmup {args.warmup} steps")
+    for t in range(args.warmup):
+        step(t, False)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for t in range(args.warmup, args.warmup + args.steps):
+        step(t, True)
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = t_start.elapsed_time(t_stop) / args.steps
+    dec_ms = [e0.elapsed_time(e1) for e0, e1, _ in dev_ev]
+    dec_bytes = [decode_bytes(w, lens)[0] for _, _, lens in dev_ev]
+    avg_dec_ms = float(np.mean(dec_ms))
+    avg_bytes = float(np.mean(dec_bytes))
+    log(f"step {step_ms:.4f} ms (host wall {1e3 * wall / args.steps:.4f} ms), decode {avg_dec_ms:.4f} ms "
+        f"(min {min(dec_ms):.4f}, max {max(dec_ms):.4f})")
+    value = avg_bytes / (step_ms * 1e-3) / 1e9
+    achieved = avg_bytes / (avg_dec_ms * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.kv_dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD_NAMES.get(w.name, w.name),
+            "batch": B, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim, "block_size": w.block_size, "kv_dtype": w.kv_dtype,
+            "mean_context": float(np.mean(d.lengths)), "sliding_window": w.window,
+            "num_splits": args.splits, "replicas": len(reps),
+        },
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "seq_heads_per_s": round(B * w.num_q_heads / (step_ms * 1e-3), 1),
+        "decode_ms": round(avg_dec_ms, 5),
+        "decode_GBps": round(achieved, 2),
+        "decode_seq_heads_per_s": round(B * w.num_q_heads / (avg_dec_ms * 1e-3), 1),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": args.traffic,
+            "kernel": "paged_attention_decode (decode_kernel + merge_kernel)",
+        },
+        "cpu_baseline": None,
+    }
+    return res, w, d
+
+
+def cpu_baseline(w, d, budget_s):
+    """The oracle, as it stands, on the first sequences of the same workload
+    (state built outside the timed region), scaled to GB/s."""
+    import threadpoolctl
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from oracle import BlockManager, PoolModel, decode_attention
+    B = len(d.lengths)
+    # size the sample: time one sequence first
+    n = 1
+    elapsed = 0.0
+    while True:
+        sub = d.lengths[:n]
+        nb = sum(-(-int(L) // w.block_size) for L in sub)
+        bm = BlockManager(nb, w.block_size)
+        kw = {}
+        if w.kv_dtype == "fp8":
+            raise RuntimeError("cpu baseline for FP8 not sized here")
+        pool = PoolModel(1, nb, w.num_kv_heads, w.block_size, w.head_dim, w.kv_dtype, **kw)
+        seqs = []
+        for b, L in enumerate(sub):
+            s = bm.alloc()
+            slots, _ = bm.append(s, int(L))
+            kb, vb = wl.kv_tokens_bits(w, (1, b), int(L))
+            pool.append(0, kb, vb, w.src_dtype, slots)
+            seqs.append(s)
+        tables, lens = bm.export(seqs, max(-(-int(L) // w.block_size) for L in sub))
+        q = wl.q_bits(w)[:n]
+        t0 = time.perf_counter()
+        decode_attention(pool, 0, q, w.q_dtype, tables, lens, 1.0 / math.sqrt(w.head_dim), w.window)
+        elapsed = time.perf_counter() - t0
+        if elapsed >= budget_s or n >= B:
+            break
+        per = elapsed / n
+        n = min(B, max(n + 1, int(budget_s / max(per, 1e-6))))
+    nbytes, _ = decode_bytes(w, d.lengths[:n])
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    return {
+        "value": round(nbytes / elapsed / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"first {n} of {B} sequences of the same workload, one decode call, "
+                  f"{elapsed:.1f} s (float64 NumPy gather + textbook attention)",
+        "seq_heads_per_s": round(n * w.num_q_heads / elapsed, 2),
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c3", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--splits", type=int, default=0, help="num_splits passed to decode (0 = automatic)")
+    ap.add_argument("--replicas", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", type=float, default=None,
+                    help="HBM bytes per decode call from rocprofv3 counters (GB)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the decode path runs on a single MI355X; "
+              "multi-GPU runs are not part of this benchmark", file=sys.stderr)
+        sys.exit(2)
+    res, w, d = run(args)
+    if not args.no_cpu_baseline and w.kv_dtype != "fp8":
+        log("cpu baseline (oracle)")
+        res["cpu_baseline"] = cpu_baseline(w, d, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -524,16 +524,18 @@ struct Decoder {
         Tile t;
         load_tile(t, kblk, vblk, st, i, kg);
         const f32x4 S = qk(t, qo);
+        // Masking is branch-free: a branch between the QK MFMAs and the first
+        // read of S would leave the MFMA-to-VALU wait states to the branch
+        // target.
         float s[4];
-        const bool whole = t0 >= lo && t0 + 16 <= L;
         bool valid[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int32_t tok = t0 + 4 * kg + r;
-          valid[r] = whole || (tok >= lo && tok < L);
+          valid[r] = tok >= lo && tok < L;
           s[r] = valid[r] ? S[r] * P.scale_log2 : -INFINITY;
         }
-        if (!whole) mask_v(t, valid);
+        mask_v(t, valid);
         float bmax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
         bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
         bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
@@ -706,8 +708,10 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams P) {
   for (int h0 = 0; h0 < P.group; h0 += HPI) {
     const int h = h0 + hl;
     if (h >= P.group) continue;
+    // wavefronts with an empty range (more wavefronts than blocks) hold no piece
     float M = -INFINITY;
     for (int64_t wv = wf; wv <= wl; ++wv) {
+      if (range_start(wv + 1, T, W) == range_start(wv, T, W)) continue;
       const int which = wv == wf ? first_which : 0;
       M = fmaxf(M, P.ws_ml[((wv * 2 + which) * P.group + h) * 2]);
     }
@@ -715,6 +719,7 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams P) {
     float Lsum = 0.f;
     if (M != -INFINITY) {
       for (int64_t wv = wf; wv <= wl; ++wv) {
+        if (range_start(wv + 1, T, W) == range_start(wv, T, W)) continue;
         const int which = wv == wf ? first_which : 0;
         const int64_t slot = (wv * 2 + which) * P.group + h;
         const f32x2 ml = *reinterpret_cast<const f32x2*>(P.ws_ml + slot * 2);
