@@ -29,6 +29,14 @@ class PagedKVOOM(PagedKVError):
     pass
 
 
+# A process must hold exactly one HIP runtime.  torch ships its own copy of
+# libamdhip64 / libhsa-runtime64 (same sonames as /opt/rocm's) and loads it by
+# a name that does not match an already loaded /opt/rocm copy, so loading this
+# library first would leave two runtimes in the process, and the second one to
+# initialise finds no device.  Importing torch first makes the library's
+# libamdhip64.so.7 dependency resolve to torch's runtime.
+import torch  # noqa: E402,F401
+
 if not os.path.exists(_LIB_PATH):
     raise ImportError(
         f"{_LIB_PATH} is missing: build it with `python paged_kv_cache_406_amd/build.py` "

@@ -221,3 +221,17 @@ def test_decode_argument_validation_on_host():
         assert e.value.status == P.PKV_E_UNSUPPORTED
     finally:
         P.kv_pool_destroy(h)
+
+
+def test_one_hip_runtime_in_process():
+    # Loading the library must not bring a second HIP runtime into a process
+    # that also uses torch (two runtimes: the second one finds no device).
+    import subprocess
+    import sys
+    code = ("import paged_kv_cache_406_amd, torch\n"
+            "maps = open('/proc/self/maps').read().splitlines()\n"
+            "libs = {l.split()[-1] for l in maps if 'libamdhip64' in l}\n"
+            "print(len(libs))\n")
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
+    assert res.returncode == 0, res.stderr
+    assert res.stdout.strip() == "1", res.stdout
