@@ -40,6 +40,9 @@ WORKLOAD_NAMES = {
     "c2_bs32": "llama2-7b-mha-decode-layer (B=64, 32/32 heads, d=128, fp16 KV, block 32)",
     "c2_bs128": "llama2-7b-mha-decode-layer (B=64, 32/32 heads, d=128, fp16 KV, block 128)",
     "c3": "llama2-70b-gqa-decode-layer (B=128, 64/8 heads, d=128, bf16 KV, block 16, lognormal lengths)",
+    "c4": "prefix-shared-decode (B=256 forks of a 2000-token prefix + private suffix U[1,512], 32/8 heads, "
+          "d=128, bf16 KV, block 16; each step forks a branch per sequence, appends with copy-on-write, "
+          "decodes the branches)",
     "c5": "long-context-128k-decode (B=4, L=131072, 64/8 heads, d=128, bf16 KV, block 16)",
     "c5_fp8": "long-context-128k-decode-fp8 (B=4, L=131072, 64/8 heads, d=128, FP8-E4M3 KV, block 16)",
     "c5w": "long-context-128k-window-4096 (B=4, L=131072, 64/8 heads, d=128, bf16 KV, block 16)",
@@ -49,6 +52,14 @@ WORKLOAD_NAMES = {
 def log(msg):
     sys.stderr.write(f"[bench] {msg}\n")
     sys.stderr.flush()
+
+
+def unique_kv_bytes(w, lengths):
+    """KV bytes of the distinct tokens one decode of the prefix-shared workload
+    reads: the shared prefix once, every private suffix once."""
+    eb = wl.ELEM_BYTES[w.kv_dtype]
+    per_tok = w.num_kv_heads * 2 * w.head_dim * eb
+    return (w.prefix_len + sum(int(L) - w.prefix_len for L in lengths)) * per_tok
 
 
 def decode_bytes(w, lengths):
@@ -80,12 +91,30 @@ class Replica:
                                   d.num_blocks, w.kv_dtype, free_order=order, **scales)
         h = self.pool.handle
         self.seqs = []
-        for b, L in enumerate(d.lengths):
-            s = P.block_table_alloc(h)
-            slots, _ = P.block_table_append(h, s, int(L))
-            kd, vd = kv_cache[b]
-            P.paged_kv_append(h, 0, kd, vd, w.src_dtype, torch.from_numpy(slots).cuda(), int(L))
-            self.seqs.append(s)
+        if w.lengths_kind == "prefix":
+            # one root holds the shared prefix; every sequence is a fork of it
+            # (refcount B on the prefix blocks) with its own suffix
+            root = P.block_table_alloc(h)
+            slots, _ = P.block_table_append(h, root, w.prefix_len)
+            kd, vd = kv_cache["prefix"]
+            P.paged_kv_append(h, 0, kd, vd, w.src_dtype, torch.from_numpy(slots).cuda(), w.prefix_len)
+            self.seqs = P.block_table_fork_batch(h, [root] * len(d.lengths)).tolist()
+            P.block_table_free(h, root)
+            for b, s in enumerate(self.seqs):
+                n = int(d.suffix[b])
+                slots, cows = P.block_table_append(h, s, n)
+                if cows:
+                    pairs = torch.tensor(cows, dtype=torch.int32).cuda()
+                    P.kv_pool_copy_blocks(h, pairs, len(cows))
+                kd, vd = kv_cache[b]
+                P.paged_kv_append(h, 0, kd, vd, w.src_dtype, torch.from_numpy(slots).cuda(), n)
+        else:
+            for b, L in enumerate(d.lengths):
+                s = P.block_table_alloc(h)
+                slots, _ = P.block_table_append(h, s, int(L))
+                kd, vd = kv_cache[b]
+                P.paged_kv_append(h, 0, kd, vd, w.src_dtype, torch.from_numpy(slots).cuda(), int(L))
+                self.seqs.append(s)
         self.seq_arr = np.asarray(self.seqs, dtype=np.int32)
         B = len(self.seqs)
         self.max_blocks = max_blocks
@@ -105,23 +134,30 @@ def build_state(args, P, torch):
     steps_total = args.steps + args.warmup
     # headroom: every sequence may take one new block per block_size steps
     extra = w.batch * (-(-steps_total // w.block_size) + 1)
+    if w.lengths_kind == "prefix":
+        extra = 2 * w.batch      # each step's branches take one block each, freed at its end
     d = wl.draw(w, extra_blocks=extra)
     bytes0, kv0 = decode_bytes(w, d.lengths)
+    if w.lengths_kind == "prefix":
+        kv0 = unique_kv_bytes(w, d.lengths)
     reps = args.replicas or max(1, math.ceil(2 * 2 ** 30 / kv0))
     log(f"workload {w.name}: B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} D={w.head_dim} "
         f"bs={w.block_size} kv={w.kv_dtype} pool={d.num_blocks} blocks, KV bytes/call={kv0/1e9:.3f} GB, "
         f"replicas={reps}")
     t0 = time.time()
-    kv_cache = []
+    kv_cache = {}
     absmax_k = np.zeros((w.num_kv_heads, w.head_dim), np.float32)
     absmax_v = np.zeros((w.num_kv_heads, w.head_dim), np.float32)
-    for b, L in enumerate(d.lengths):
-        kb, vb = wl.kv_tokens_bits(w, (1, b), int(L))
+    streams = [(b, (1, b), int(L)) for b, L in enumerate(d.lengths)]
+    if w.lengths_kind == "prefix":
+        streams = [("prefix", (3,), w.prefix_len)] + [(b, (1, b), int(n)) for b, n in enumerate(d.suffix)]
+    for b, stream_id, L in streams:
+        kb, vb = wl.kv_tokens_bits(w, stream_id, L)
         if w.kv_dtype == "fp8":
             absmax_k = np.maximum(absmax_k, np.abs(wl.bits_as_f32(kb, w.src_dtype)).max(axis=0))
             absmax_v = np.maximum(absmax_v, np.abs(wl.bits_as_f32(vb, w.src_dtype)).max(axis=0))
         tdt = np.int16 if kb.dtype == np.uint16 else np.int32
-        kv_cache.append((torch.from_numpy(kb.view(tdt)).cuda(), torch.from_numpy(vb.view(tdt)).cuda()))
+        kv_cache[b] = (torch.from_numpy(kb.view(tdt)).cuda(), torch.from_numpy(vb.view(tdt)).cuda())
     scales = {}
     if w.kv_dtype == "fp8":
         ks, _ = wl.fp8_scales(absmax_k)
@@ -163,7 +199,7 @@ def run(args):
                                reps[0].d_tables, reps[0].d_lens, scale, out, "f32",
                                sliding_window=w.window, num_splits=args.splits)
     ws_bytes = P.paged_attention_workspace_size(reps[0].pool.handle, args0)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
     # pinned staging ring for the per-step metadata
     ring = []
     for _ in range(4):
@@ -171,6 +207,7 @@ def run(args):
         ring.append((buf, buf.numpy(), torch.cuda.Event()))
     mb = reps[0].max_blocks
     dev_ev = []
+    prefix = w.lengths_kind == "prefix"
 
     def step(t, record):
         rep = reps[t % len(reps)]
@@ -181,9 +218,17 @@ def run(args):
         cows_np = npb[2 * B: 4 * B].reshape(B, 2)
         tables_np = npb[4 * B: 4 * B + B * mb].reshape(B, mb)
         lens_np = npb[4 * B + B * mb:]
-        _, cows = P.block_table_append_batch(h, rep.seq_arr, slots_out=slots_np, cow_out=cows_np)
-        P.block_table_export(h, rep.seq_arr, mb, tables_out=tables_np, lens_out=lens_np)
-        rep.lengths += 1
+        if prefix:
+            # a sampling branch per sequence: fork, append (copy-on-write of the
+            # shared partial last block), decode, free
+            seqs = P.block_table_fork_batch(h, rep.seq_arr)
+            lens_now = rep.lengths + 1
+        else:
+            seqs = rep.seq_arr
+            rep.lengths += 1
+            lens_now = rep.lengths
+        _, cows = P.block_table_append_batch(h, seqs, slots_out=slots_np, cow_out=cows_np)
+        P.block_table_export(h, seqs, mb, tables_out=tables_np, lens_out=lens_np)
         rep.meta.copy_(buf, non_blocking=True)
         ev.record(stream)
         if len(cows):
@@ -198,9 +243,13 @@ def run(args):
             e0.record(stream)
             P.paged_attention_decode(h, a, sptr)
             e1.record(stream)
-            dev_ev.append((e0, e1, rep.lengths.copy()))
+            dev_ev.append((e0, e1, lens_now.copy()))
         else:
             P.paged_attention_decode(h, a, sptr)
+        if prefix:
+            # host bookkeeping only: stream order keeps this step's kernels ahead
+            # of any later reuse of the freed blocks
+            P.block_table_free_batch(h, seqs)
 
     log(f"warmup {args.warmup} steps")
     for t in range(args.warmup):
@@ -220,7 +269,13 @@ def run(args):
     dec_ms = [e0.elapsed_time(e1) for e0, e1, _ in dev_ev]
     dec_bytes = [decode_bytes(w, lens)[0] for _, _, lens in dev_ev]
     avg_dec_ms = float(np.mean(dec_ms))
-    avg_bytes = float(np.mean(dec_bytes))
+    logical_bytes = float(np.mean(dec_bytes))
+    avg_bytes = logical_bytes
+    if prefix:
+        # HBM bound on the distinct bytes: the shared prefix is one set of blocks
+        # (its repeated reads are served by the caches); the other terms as usual
+        kv_logical = float(np.mean([decode_bytes(w, lens)[1] for _, _, lens in dev_ev]))
+        avg_bytes = logical_bytes - kv_logical + float(np.mean([unique_kv_bytes(w, lens) for _, _, lens in dev_ev]))
     log(f"step {step_ms:.4f} ms (host wall {1e3 * wall / args.steps:.4f} ms), decode {avg_dec_ms:.4f} ms "
         f"(min {min(dec_ms):.4f}, max {max(dec_ms):.4f})")
     value = avg_bytes / (step_ms * 1e-3) / 1e9
@@ -257,10 +312,13 @@ def run(args):
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": args.traffic,
-            "kernel": "paged_attention_decode (decode_kernel + merge_kernel)",
+            "kernel": "paged_attention_decode (decode_kernel, log-sum-exp merge inside)",
         },
         "cpu_baseline": None,
     }
+    if prefix:
+        res["logical_decode_GBps"] = round(logical_bytes / (avg_dec_ms * 1e-3) / 1e9, 2)
+        res["bytes_basis"] = "unique (shared prefix counted once)"
     return res, w, d
 
 
@@ -331,7 +389,7 @@ def main():
               "multi-GPU runs are not part of this benchmark", file=sys.stderr)
         sys.exit(2)
     res, w, d = run(args)
-    if not args.no_cpu_baseline and w.kv_dtype != "fp8":
+    if not args.no_cpu_baseline and w.kv_dtype != "fp8" and w.lengths_kind != "prefix":
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(w, d, args.cpu_budget)
     print(json.dumps(res), flush=True)

@@ -162,6 +162,17 @@ pkv_status block_table_fork(kv_pool* pool, int32_t parent, int32_t* child_out);
  * goes to the back of the free queue.  The id becomes invalid. */
 pkv_status block_table_free(kv_pool* pool, int32_t seq);
 
+/* n forks at once: children_out[i] receives a new sequence sharing every
+ * block of parents[i] (a parent may appear several times).  Children get
+ * consecutive ids in order.  All or nothing: an unknown parent changes
+ * nothing.  children_out: host int32 [n]. */
+pkv_status block_table_fork_batch(kv_pool* pool, const int32_t* parents, int32_t n,
+                                  int32_t* children_out);
+
+/* n frees at once, in the given order, each as block_table_free.  All or
+ * nothing: an unknown or repeated id changes nothing. */
+pkv_status block_table_free_batch(kv_pool* pool, const int32_t* seqs, int32_t n);
+
 /* Copy a sequence's table (up to cap entries) and report its block count and
  * token length.  blocks_out may be NULL when cap == 0. */
 pkv_status block_table_get(const kv_pool* pool, int32_t seq, int32_t* blocks_out,
@@ -203,26 +214,32 @@ typedef struct {
   int32_t num_q_heads;          /* Hq, a multiple of num_kv_heads, Hq / Hkv <= 16 */
   int32_t max_blocks_per_seq;   /* row length of block_tables */
   int32_t sliding_window;       /* 0: off; W > 0: keys L-W .. L-1 only */
-  int32_t num_splits;           /* 0: automatic; 1: single pass, one wavefront per
+  int32_t num_splits;           /* <= 16384.  0: automatic; 1: single pass, one wavefront per
                                    (sequence, KV head), no workspace; n >= 2: the
-                                   blocks of all (KV head, sequence) pairs, laid end
-                                   to end, are cut into n equal ranges, one per
-                                   wavefront, and partial results are combined by a
-                                   log-sum-exp merge */
-  const void* q;                /* device [B][Hq][head_dim] */
+                                   work units of all (KV head, sequence) pairs (a
+                                   unit is max(block_size, 16 / 32 / 64) tokens for
+                                   fp32 / fp16, bf16 / FP8 pools), laid end to end,
+                                   are cut into n equal ranges, one per wavefront,
+                                   and the pieces of a sequence split between ranges
+                                   are combined by a log-sum-exp merge */
+  const void* q;                /* device [B][Hq][head_dim], 16-byte aligned */
   int32_t q_dtype;              /* PKV_F32 for an fp32 pool, PKV_F16 for fp16,
                                    PKV_BF16 for bf16 and FP8 pools */
   const int32_t* block_tables;  /* device int32 [B][max_blocks_per_seq] */
   const int32_t* context_lens;  /* device int32 [B]: tokens including the new one */
   float scale;                  /* multiplies q.k; 1/sqrt(head_dim) by convention */
-  void* out;                    /* device [B][Hq][head_dim] */
+  void* out;                    /* device [B][Hq][head_dim], 16-byte aligned */
   int32_t out_dtype;            /* PKV_F32 (recommended), PKV_F16 or PKV_BF16 */
   void* workspace;              /* device, caller-owned, 256-byte aligned */
   size_t workspace_bytes;       /* >= paged_attention_workspace_size() */
 } paged_decode_args;
 
 /* Workspace paged_attention_decode needs for these arguments (0 for a single
- * pass).  For num_splits == 0 this queries the current device. */
+ * pass).  For num_splits == 0 this queries the current device.
+ * The workspace holds the partial results of sequences whose blocks are
+ * split over several wavefronts; it needs no initialisation.  One workspace
+ * serves one call at a time: calls that may overlap (other streams)
+ * need their own. */
 pkv_status paged_attention_workspace_size(const kv_pool* pool, const paged_decode_args* args,
                                           size_t* bytes_out);
 

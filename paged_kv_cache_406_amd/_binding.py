@@ -83,6 +83,8 @@ _SIGS = {
     "block_table_append_batch": (c_i32, [P_pool, P_i32, c_i32, P_i64, P_copy, P_i32]),
     "block_table_fork": (c_i32, [P_pool, c_i32, P_i32]),
     "block_table_free": (c_i32, [P_pool, c_i32]),
+    "block_table_fork_batch": (c_i32, [P_pool, P_i32, c_i32, P_i32]),
+    "block_table_free_batch": (c_i32, [P_pool, P_i32, c_i32]),
     "block_table_get": (c_i32, [P_pool, c_i32, P_i32, c_i32, P_i32, P_i32]),
     "block_table_export": (c_i32, [P_pool, P_i32, c_i32, c_i32, P_i32, P_i32]),
     "kv_pool_copy_blocks": (c_i32, [P_pool, c_vp, c_i32, c_vp]),
@@ -225,6 +227,19 @@ def block_table_fork(pool, parent) -> int:
 
 def block_table_free(pool, seq) -> None:
     _check(_lib.block_table_free(pool, seq))
+
+
+def block_table_fork_batch(pool, parents):
+    """Children (int32 [n]) of the given parents, in order."""
+    par, par_p = _i32_array(parents)
+    out = np.zeros(max(len(par), 1), dtype=np.int32)
+    _check(_lib.block_table_fork_batch(pool, par_p, len(par), out.ctypes.data_as(P_i32)))
+    return out[:len(par)]
+
+
+def block_table_free_batch(pool, seqs) -> None:
+    arr, arr_p = _i32_array(seqs)
+    _check(_lib.block_table_free_batch(pool, arr_p, len(arr)))
 
 
 def block_table_get(pool, seq):

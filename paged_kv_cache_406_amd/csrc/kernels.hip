@@ -5,10 +5,10 @@
 //                      quantise-on-write with per-channel inverse scales)
 //   copy_blocks_kernel whole-block copies for copy-on-write
 //   decode_kernel      decode attention over the paged cache: per-wavefront
-//                      ranges of (KV head, sequence, block) work, QK^T and PV
-//                      on MFMA, online softmax in registers
-//   merge_kernel       log-sum-exp merge of the partial results of sequences
-//                      whose blocks were split across wavefronts
+//                      ranges of (KV head, sequence, work unit), QK^T and PV
+//                      on MFMA, online softmax in registers, and the
+//                      log-sum-exp merge of sequences whose units were split
+//                      across wavefronts (done by the last piece to finish)
 //
 // Pages followed: "AI 陪读顶会论文（三）：KV Cache 显存占用计算与 PagedAttention
 // 原理拆解" (section "为什么自回归解码…必须使用 KV Cache": the attention
@@ -20,39 +20,44 @@
 //
 // Design notes (gfx950)
 //  * Decode is bound by HBM reads: every KV byte is used once per call.  One
-//    wavefront owns a (KV head, sequence, block range); each 16-token
-//    sub-tile of K and V goes from HBM straight into MFMA operand registers
-//    and is used for all G query heads of the group at once (the GQA reuse).
-//  * QK^T: S[16 tokens][16 heads] += K[16 tokens][k] * Q^T[k][16 heads] with
-//    v_mfma_f32_16x16x16 (bf16 / f16) or 16x16x4 (f32).  Query heads beyond G
-//    are zero columns.  The S layout (lane = head column, 4 token rows per
-//    lane) is exactly the B operand PV needs, so P never moves between lanes.
-//  * PV: O^T[16 dims][16 heads] += V^T[16 dims][16 tokens] * P^T[16 tokens][16 heads].
-//    V is stored channel-major inside a block so that a lane's 4 tokens of one
+//    wavefront owns a (KV head, sequence, unit range).  A sub-tile of 16
+//    (fp32), 32 (fp16 / bf16) or 64 (FP8) tokens of K and V goes from HBM
+//    straight into MFMA operand registers with 16-byte loads in every lane
+//    and is used for all G query heads of the group at once (the GQA reuse);
+//    the next sub-tile's loads are issued before the current one is scored
+//    (two register buffers).
+//  * QK^T: S_t[16 tokens][16 heads] = K_t[16 tokens][D] * Q^T[D][16 heads] on
+//    v_mfma_f32_16x16x32 (bf16 / f16; FP8 codes widened exactly to bf16) or
+//    16x16x4 (f32).  Query heads beyond G are zero columns.  The rows of the
+//    QK tiles are assigned to tokens so that every lane ends up holding the
+//    scores of exactly the 8 (16) consecutive tokens whose V it loaded, which
+//    is the B operand of PV: P never moves between lanes.
+//  * PV: O^T[16 dims][16 heads] += V^T[16 dims][32 tokens] * P^T[32 tokens][16 heads].
+//    V is stored channel-major inside a block so that a lane's tokens of one
 //    channel are contiguous.  bf16 P is split into hi + lo bf16 parts (two
 //    MFMAs) so the rounding of P stays far below fp32 accumulation error.
 //  * The max of each head's scores is shared by the 4 lanes holding that head
 //    (two lane exchanges); sums stay per lane until the end.
-//  * Work split: all blocks of all (KV head, sequence) pairs are laid end to
-//    end (KV-head major) and cut into W equal ranges, one per wavefront.  A
-//    range that covers a whole sequence writes the final output; the pieces of
-//    a sequence that straddles ranges are written as (unnormalised o, max,
-//    sum) and combined by merge_kernel.  Workgroups are remapped so that each
-//    XCD (one L2) gets a contiguous run of ranges.
+//  * Work split: the sub-tile-aligned units of all (KV head, sequence) pairs
+//    are laid end to end (KV-head major) and cut into W equal ranges, one per
+//    wavefront.  A range that covers a whole sequence writes the final
+//    output; a piece of a sequence that straddles ranges is written as
+//    (unnormalised o, max, sum) and counted, and the wavefront that finishes
+//    the last piece of that sequence merges them.  Workgroups are remapped so
+//    that each XCD (one L2) gets a contiguous run of ranges.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdint>
 #include <mutex>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #include "pool_internal.h"
 
 namespace pkv {
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -118,16 +123,6 @@ template <> __device__ __forceinline__ float src_to_f32<KV_F16>(const uint8_t* p
 }
 template <> __device__ __forceinline__ float src_to_f32<KV_BF16>(const uint8_t* p, int64_t idx) {
   return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p)[idx]);
-}
-
-// four E4M3 codes (one dword) -> four bf16 (exact: every E4M3 value is a bf16 value)
-__device__ __forceinline__ s16x4 e4m3x4_to_bf16x4(uint32_t codes) {
-  bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, false);
-  bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, true);
-  s16x4 r;
-  __builtin_memcpy(&r, &lo, 4);
-  __builtin_memcpy(reinterpret_cast<char*>(&r) + 4, &hi, 4);
-  return r;
 }
 
 // ---------------------------------------------------------------------------
@@ -210,6 +205,10 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* kc, uint8_t* 
 // ---------------------------------------------------------------------------
 // decode
 // ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
 struct DecodeParams {
   const uint8_t* kc;
   const uint8_t* vc;
@@ -219,20 +218,39 @@ struct DecodeParams {
   uint8_t* out;
   const int32_t* tables;
   const int32_t* lens;
-  float* ws_o;    // [W][2][G][D]
-  float* ws_ml;   // [W][2][G][2]
+  float* ws_o;        // [W][2][G][D] unnormalised partial outputs
+  float* ws_ml;       // [W][2][G][2] partial (max, sum), log2 domain
+  int4* ws_job;       // [Hkv][B] merge job of each (KV head, sequence): {first range,
+                      // pieces, slot of the first piece, 0}; pieces = 0: nothing to merge
   int64_t num_blocks;
   int32_t layer, batch, hq, hkv, group, max_blocks, window, out_dtype;
-  int32_t num_waves;   // W (range mode)
-  int32_t single;      // 1: one wavefront per (sequence, KV head)
+  int32_t num_waves;  // W: wavefront ranges (range mode)
+  int32_t single;     // 1: one wavefront per (KV head, sequence)
   int32_t xcd_remap;
-  float scale_log2;    // scale * log2(e)
+  float scale_log2;   // scale * log2(e)
 };
 
-// Blocks of sequence b that the query attends (window applied).
-template <int BS>
-__device__ __forceinline__ void seq_extent(const DecodeParams& P, int b, int32_t* L_out,
-                                           int32_t* lo_out, int32_t* first_out, int32_t* nblk_out) {
+// Tokens per sub-tile: the amount one wavefront loads and scores at a time.
+// Each lane group (16 lanes) holds TT/4 consecutive tokens of V, which is
+// 16 bytes for every element size.
+template <int KV> struct SubTile;
+template <> struct SubTile<KV_F32> { static constexpr int TT = 16; };
+template <> struct SubTile<KV_F16> { static constexpr int TT = 32; };
+template <> struct SubTile<KV_BF16> { static constexpr int TT = 32; };
+template <> struct SubTile<KV_FP8> { static constexpr int TT = 64; };
+
+template <int KV, int BS>
+struct Units {
+  static constexpr int TT = SubTile<KV>::TT;
+  static constexpr int U = BS > TT ? BS : TT;  // tokens per work unit (whole blocks, whole sub-tiles)
+  static constexpr int UB = U / BS;            // blocks per unit
+};
+
+// Attended range of sequence b: L tokens (clamped to the table), first key
+// lo (window), first block, and the number of work units from that block on.
+template <int BS, int U>
+__device__ __forceinline__ void seq_extent(const DecodeParams& P, int b, int32_t* L_out, int32_t* lo_out,
+                                           int32_t* first_out, int32_t* nunits_out) {
   int32_t L = P.lens[b];
   const int32_t cap = P.max_blocks * BS;
   L = L < 0 ? 0 : (L > cap ? cap : L);
@@ -241,12 +259,12 @@ __device__ __forceinline__ void seq_extent(const DecodeParams& P, int b, int32_t
   *L_out = L;
   *lo_out = lo;
   *first_out = first;
-  *nblk_out = L > lo ? (L + BS - 1) / BS - first : 0;
+  *nunits_out = L > lo ? (L - first * BS + U - 1) / U : 0;
 }
 
-// Exclusive prefix sums of the per-sequence block counts into C[0..B] (LDS).
-template <int BS>
-__device__ void scan_block_counts(const DecodeParams& P, int32_t* C) {
+// Exclusive prefix sums of the per-sequence unit counts into C[0..B] (LDS).
+template <int BS, int U>
+__device__ void scan_units(const DecodeParams& P, int32_t* C) {
   __shared__ int32_t part[256];
   const int tid = threadIdx.x;
   const int per = (P.batch + 255) / 256;
@@ -254,9 +272,10 @@ __device__ void scan_block_counts(const DecodeParams& P, int32_t* C) {
   const int b1 = min(P.batch, b0 + per);
   int32_t local = 0;
   for (int b = b0; b < b1; ++b) {
-    int32_t L, lo, first, nb;
-    seq_extent<BS>(P, b, &L, &lo, &first, &nb);
-    local += nb;
+    int32_t L, lo, first, nu;
+    seq_extent<BS, U>(P, b, &L, &lo, &first, &nu);
+    C[b] = nu;
+    local += nu;
   }
   part[tid] = local;
   __syncthreads();
@@ -268,10 +287,9 @@ __device__ void scan_block_counts(const DecodeParams& P, int32_t* C) {
   }
   int32_t run = part[tid] - local;
   for (int b = b0; b < b1; ++b) {
-    int32_t L, lo, first, nb;
-    seq_extent<BS>(P, b, &L, &lo, &first, &nb);
+    const int32_t nu = C[b];
     C[b] = run;
-    run += nb;
+    run += nu;
   }
   if (tid == 255) C[P.batch] = part[255];
   __syncthreads();
@@ -279,7 +297,7 @@ __device__ void scan_block_counts(const DecodeParams& P, int32_t* C) {
 
 __device__ __forceinline__ int64_t range_start(int64_t w, int64_t T, int64_t W) { return w * T / W; }
 
-// Largest w with range_start(w) <= x (the wavefront whose range holds x).
+// The wavefront whose range holds unit x (every range is non-empty: W <= T).
 __device__ __forceinline__ int64_t wave_of(int64_t x, int64_t T, int64_t W) {
   return ((x + 1) * W - 1) / T;
 }
@@ -289,275 +307,421 @@ __device__ __forceinline__ T uniform(T v) {
   return __builtin_amdgcn_readfirstlane(v);
 }
 
-// Operand / load types per KV dtype.
-template <int KV> struct Ops;
-template <> struct Ops<KV_F32> {
-  typedef float qop;          // one k-step of 16x16x4 f32
-  typedef uint4 vload;        // 4 tokens of one channel
-  static constexpr int kpl = 1;
-};
-template <> struct Ops<KV_F16> {
-  typedef f16x4 qop;
-  typedef uint2 vload;
-  static constexpr int kpl = 4;
-};
-template <> struct Ops<KV_BF16> {
-  typedef s16x4 qop;
-  typedef uint2 vload;
-  static constexpr int kpl = 4;
-};
-template <> struct Ops<KV_FP8> {
-  typedef s16x4 qop;
-  typedef uint32_t vload;
-  static constexpr int kpl = 4;
-};
+__device__ __forceinline__ void store4(const DecodeParams& P, int64_t off, const f32x4& o) {
+  if (P.out_dtype == PKV_F32) {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(P.out) + off) = o;
+  } else if (P.out_dtype == PKV_BF16) {
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(P.out) + off) =
+        make_uint2(f32_to_bf16_bits_rne(o[0]) | (f32_to_bf16_bits_rne(o[1]) << 16),
+                   f32_to_bf16_bits_rne(o[2]) | (f32_to_bf16_bits_rne(o[3]) << 16));
+  } else {
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(P.out) + off) =
+        make_uint2(f32_to_f16_bits(o[0]) | (f32_to_f16_bits(o[1]) << 16),
+                   f32_to_f16_bits(o[2]) | (f32_to_f16_bits(o[3]) << 16));
+  }
+}
 
+template <int D>
+__device__ __forceinline__ void write_zero_rows(const DecodeParams& P, int b, int g, int lane) {
+  const int64_t row0 = ((int64_t)b * P.hq + (int64_t)g * P.group) * D;
+  const int64_t n = (int64_t)P.group * D;
+  for (int64_t e = lane; e < n; e += 64) {
+    if (P.out_dtype == PKV_F32) reinterpret_cast<float*>(P.out)[row0 + e] = 0.f;
+    else reinterpret_cast<uint16_t*>(P.out)[row0 + e] = 0;
+  }
+}
+
+// 16 bytes as 8 x 16-bit MFMA operand elements
+template <typename V8>
+__device__ __forceinline__ V8 as8(const uint4& w) {
+  V8 r;
+  __builtin_memcpy(&r, &w, 16);
+  return r;
+}
+
+// 8 E4M3 codes (two dwords) -> 8 bf16 (exact: every E4M3 value is a bf16 value)
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t a, uint32_t b) {
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(a, 1.0f, false);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(a, 1.0f, true);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b, 1.0f, false);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b, 1.0f, true);
+  bf16x8 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+// One wavefront's view of the decode of a (KV head g, sequence b) piece.
+//
+// Lane l has i = l % 16 and kg = l / 16 (its lane group).  A sub-tile holds
+// TT tokens; lane group kg owns the TPG = TT/4 consecutive tokens
+// [TPG*kg, TPG*kg + TPG) of it.  Scores come from NQT = TT/16 MFMA tiles
+// S_t[16 rows][16 heads]; row 4*kg + r of tile t is token TPG*kg + 4*t + r, so
+// the output layout of S_t (lane (head, kg) holds rows 4*kg .. 4*kg+3) leaves
+// every lane holding exactly the scores of its own lane group's tokens, which
+// is the B operand the P.V MFMA needs, in the token order of its 16-byte V
+// loads.  Query heads are MFMA columns (heads >= G are zero columns).
 template <int KV, int D, int BS>
 struct Decoder {
   static constexpr int EB = Elem<KV>::bytes;
-  static constexpr int X = 16 / EB;          // channels per 16-byte K group
-  static constexpr int NCH = D / (4 * X);    // 16-byte K loads per lane per sub-tile
-  static constexpr int NV = D / 16;          // V loads (channel groups) per lane per sub-tile
-  static constexpr int STEPS = D / (4 * Ops<KV>::kpl);  // QK MFMA steps
-  static constexpr int SUB = BS / 16;        // 16-token sub-tiles per block
-  typedef typename Ops<KV>::qop qop;
-  typedef typename Ops<KV>::vload vload;
+  static constexpr int X = 16 / EB;                // channels per 16-byte K group
+  static constexpr int TT = SubTile<KV>::TT;
+  static constexpr int TPG = TT / 4;               // tokens per lane group
+  static constexpr int NQT = TT / 16;              // QK tiles per sub-tile
+  static constexpr int NKJ = D / (4 * X);          // K loads per lane per QK tile
+  static constexpr int NKL = NQT * NKJ;            // K loads per lane per sub-tile
+  static constexpr int NV = D / 16;                // V loads per lane per sub-tile = O tiles
+  static constexpr int U = Units<KV, BS>::U;
+  static constexpr int UB = Units<KV, BS>::UB;
+  static constexpr int SPU = U / TT;               // sub-tiles per unit
+  static constexpr int NQ = KV == KV_F32 ? D / 4 : D / 32;  // q operands per lane
+  static constexpr int EPW = 4 / EB;               // V elements per dword
+  static constexpr int64_t TILE_BYTES = (int64_t)D * BS * EB;  // one (block, KV head) tile
 
-  // channel held by element e (0 .. D/4-1) of lane group kg's K vector
-  static __device__ __forceinline__ int chan(int kg, int e) { return (kg + 4 * (e / X)) * X + (e % X); }
+  typedef typename std::conditional<KV == KV_F32, float,
+          typename std::conditional<KV == KV_F16, f16x8, bf16x8>::type>::type qop;
 
-  // Loads this lane's q operands (head i of group g; zero for i >= G).  FP8
-  // folds the per-channel K scale into q (q'[c] = q[c] * k_scale[c]).
+  struct KTile {
+    uint4 k[NKL];
+  };
+  struct VTile {
+    uint4 v[NV];
+    int32_t tok0;  // absolute index of the sub-tile's first token
+    bool ok;       // this lane group's V block is a real block
+  };
+  // Where this lane's K rows and V tokens of one sub-tile live.
+  struct Addr {
+    const uint8_t* krow;  // this lane's first K group (channel group kg, its first row)
+    const uint8_t* vrow;  // this lane's first V row (channel i, its first token)
+    int32_t tok0;
+    bool ok;
+  };
+
+  struct State {
+    f32x4 O[NV];
+    float m;
+    float l;
+  };
+
+  // q operands of head i of group g (zero for i >= G).  Element e of operand
+  // s multiplies the same channel as element e of the K operand of step s.
+  // FP8 folds the per-channel K scale into q (q'[c] = q[c] * k_scale[c]).
   static __device__ __forceinline__ void load_q(const DecodeParams& P, int b, int g, int i, int kg,
-                                                qop (&qo)[STEPS]) {
+                                                qop (&qo)[NQ]) {
     const bool live = i < P.group;
     const int64_t row = ((int64_t)b * P.hq + (int64_t)g * P.group + (live ? i : 0)) * D;
     if constexpr (KV == KV_F32) {
       const float* q = reinterpret_cast<const float*>(P.q) + row;
 #pragma unroll
-      for (int s = 0; s < STEPS; ++s) qo[s] = live ? q[chan(kg, s)] : 0.0f;
+      for (int j = 0; j < NKJ; ++j)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) qo[4 * j + u] = live ? q[(kg + 4 * j) * 4 + u] : 0.0f;
     } else if constexpr (KV == KV_F16 || KV == KV_BF16) {
-      const uint16_t* q = reinterpret_cast<const uint16_t*>(P.q) + row;
+      const uint8_t* q = P.q + row * 2;
 #pragma unroll
-      for (int s = 0; s < STEPS; ++s) {
-        s16x4 v;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = live ? (short)q[chan(kg, 4 * s + u)] : (short)0;
-        __builtin_memcpy(&qo[s], &v, 8);
+      for (int j = 0; j < NKJ; ++j) {
+        uint4 w = *reinterpret_cast<const uint4*>(q + (kg + 4 * j) * 16);
+        if (!live) w = make_uint4(0, 0, 0, 0);
+        qo[j] = as8<qop>(w);
       }
     } else {
       const uint16_t* q = reinterpret_cast<const uint16_t*>(P.q) + row;
       const float* ks = P.k_scale + ((int64_t)P.layer * P.hkv + g) * D;
 #pragma unroll
-      for (int s = 0; s < STEPS; ++s) {
-        s16x4 v;
+      for (int j = 0; j < NKJ; ++j)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int c = chan(kg, 4 * s + u);
-          const float x = live ? bf16_bits_to_f32(q[c]) * ks[c] : 0.0f;
-          v[u] = (short)f32_to_bf16_bits_rne(x);
+        for (int h = 0; h < 2; ++h) {
+          uint32_t w[4];
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const int c = (kg + 4 * j) * 16 + 8 * h + e;
+            const float x0 = live ? bf16_bits_to_f32(q[c]) * ks[c] : 0.0f;
+            const float x1 = live ? bf16_bits_to_f32(q[c + 1]) * ks[c + 1] : 0.0f;
+            w[e / 2] = f32_to_bf16_bits_rne(x0) | (f32_to_bf16_bits_rne(x1) << 16);
+          }
+          qo[2 * j + h] = as8<qop>(make_uint4(w[0], w[1], w[2], w[3]));
         }
-        qo[s] = v;
-      }
     }
   }
 
-  struct Tile {
-    uint4 k[NCH];
-    vload v[NV];
-  };
-
-  static __device__ __forceinline__ void load_tile(Tile& t, const uint8_t* kblk, const uint8_t* vblk,
-                                                   int st, int i, int kg) {
-#pragma unroll
-    for (int j = 0; j < NCH; ++j)
-      t.k[j] = *reinterpret_cast<const uint4*>(kblk + ((int64_t)((kg + 4 * j) * BS + 16 * st + i) * X) * EB);
-#pragma unroll
-    for (int n = 0; n < NV; ++n)
-      t.v[n] = *reinterpret_cast<const vload*>(vblk + ((int64_t)(16 * n + i) * BS + 16 * st + 4 * kg) * EB);
-  }
-
-  static __device__ __forceinline__ f32x4 qk(const Tile& t, const qop (&qo)[STEPS]) {
-    f32x4 S = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (KV == KV_F32) {
-#pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        const float kf[4] = {__uint_as_float(t.k[j].x), __uint_as_float(t.k[j].y),
-                             __uint_as_float(t.k[j].z), __uint_as_float(t.k[j].w)};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) S = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[u], qo[4 * j + u], S, 0, 0, 0);
-      }
-    } else if constexpr (KV == KV_F16 || KV == KV_BF16) {
-#pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        const uint2 lo = make_uint2(t.k[j].x, t.k[j].y);
-        const uint2 hi = make_uint2(t.k[j].z, t.k[j].w);
-        qop a0, a1;
-        __builtin_memcpy(&a0, &lo, 8);
-        __builtin_memcpy(&a1, &hi, 8);
-        if constexpr (KV == KV_F16) {
-          S = __builtin_amdgcn_mfma_f32_16x16x16f16(a0, qo[2 * j], S, 0, 0, 0);
-          S = __builtin_amdgcn_mfma_f32_16x16x16f16(a1, qo[2 * j + 1], S, 0, 0, 0);
-        } else {
-          S = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a0, qo[2 * j], S, 0, 0, 0);
-          S = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a1, qo[2 * j + 1], S, 0, 0, 0);
-        }
-      }
+  // Addresses of one sub-tile.  ids: the UB physical blocks of its unit
+  // (uniform); st: sub-tile within the unit.  A lane whose block id is not a
+  // real block reads block 0 instead and its tokens are masked later.
+  static __device__ __forceinline__ Addr locate(const DecodeParams& P, int g, const int32_t (&ids)[UB], int st,
+                                                int32_t tok0, int i, int kg) {
+    int kb = 0, vb = 0, koff, voff;
+    Addr a;
+    if constexpr (UB == 1) {
+      koff = st * TT + TPG * (i >> 2) + (i & 3);
+      voff = st * TT + TPG * kg;
     } else {
-#pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        const uint32_t w4[4] = {t.k[j].x, t.k[j].y, t.k[j].z, t.k[j].w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          S = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(e4m3x4_to_bf16x4(w4[u]), qo[4 * j + u], S, 0, 0, 0);
-      }
+      kb = (TPG * (i >> 2)) / BS;
+      vb = (TPG * kg) / BS;
+      koff = (TPG * (i >> 2)) % BS + (i & 3);
+      voff = (TPG * kg) % BS;
     }
-    return S;
+    int32_t pk = ids[0], pv = ids[0];
+#pragma unroll
+    for (int u = 1; u < UB; ++u) {
+      pk = kb == u ? ids[u] : pk;
+      pv = vb == u ? ids[u] : pv;
+    }
+    const bool okk = pk >= 0 && pk < P.num_blocks;
+    const bool okv = pv >= 0 && pv < P.num_blocks;
+    const int64_t head_tile = (int64_t)P.layer * P.num_blocks * P.hkv + g;
+    a.krow = P.kc + (head_tile + (int64_t)(okk ? pk : 0) * P.hkv) * TILE_BYTES + (uint32_t)(kg * BS + koff) * 16u;
+    a.vrow = P.vc + (head_tile + (int64_t)(okv ? pv : 0) * P.hkv) * TILE_BYTES + (uint32_t)(i * BS + voff) * (uint32_t)EB;
+    a.tok0 = tok0;
+    a.ok = okv;
+    return a;
   }
 
-  // Zero the V elements of tokens r with !valid[r] (their bits may be garbage).
-  static __device__ __forceinline__ void mask_v(Tile& t, const bool (&valid)[4]) {
+  // Constant offsets from the row pointers: K group kg + 4j and row + 4t;
+  // V channel 16n + i.
+  static __device__ __forceinline__ void load_k(KTile& T, const Addr& a) {
+#pragma unroll
+    for (int t = 0; t < NQT; ++t)
+#pragma unroll
+      for (int j = 0; j < NKJ; ++j)
+        T.k[t * NKJ + j] = *reinterpret_cast<const uint4*>(a.krow + (4 * j * BS + 4 * t) * 16);
+  }
+
+  static __device__ __forceinline__ void load_v(VTile& T, const Addr& a) {
+#pragma unroll
+    for (int n = 0; n < NV; ++n) T.v[n] = *reinterpret_cast<const uint4*>(a.vrow + 16 * n * BS * EB);
+    T.tok0 = a.tok0;
+    T.ok = a.ok;
+  }
+
+  static __device__ __forceinline__ void qk(const KTile& T, const qop (&qo)[NQ], f32x4 (&S)[NQT]) {
+#pragma unroll
+    for (int t = 0; t < NQT; ++t) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < NKJ; ++j) {
+        const uint4 w = T.k[t * NKJ + j];
+        if constexpr (KV == KV_F32) {
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(w.x), qo[4 * j + 0], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(w.y), qo[4 * j + 1], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(w.z), qo[4 * j + 2], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(w.w), qo[4 * j + 3], acc, 0, 0, 0);
+        } else if constexpr (KV == KV_F16) {
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as8<f16x8>(w), qo[j], acc, 0, 0, 0);
+        } else if constexpr (KV == KV_BF16) {
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as8<bf16x8>(w), qo[j], acc, 0, 0, 0);
+        } else {
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(w.x, w.y), qo[2 * j], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(w.z, w.w), qo[2 * j + 1], acc, 0, 0, 0);
+        }
+      }
+      S[t] = acc;
+    }
+  }
+
+  // Online softmax over one scored sub-tile: probabilities p of this lane's
+  // tokens (0 where not attended), running max / sum, O rescaled.
+  static __device__ __forceinline__ void softmax(const VTile& T, const f32x4 (&S)[NQT], State& st,
+                                                 float (&p)[NQT][4], int32_t lo, int32_t L, float scale_log2,
+                                                 int kg) {
+    float s[NQT][4];
+#pragma unroll
+    for (int t = 0; t < NQT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int32_t tok = T.tok0 + TPG * kg + 4 * t + r;
+        const bool valid = T.ok && tok >= lo && tok < L;
+        s[t][r] = valid ? S[t][r] * scale_log2 : -INFINITY;
+      }
+    float bmax = s[0][0];
+#pragma unroll
+    for (int t = 0; t < NQT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) bmax = fmaxf(bmax, s[t][r]);
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+    const float m_new = fmaxf(st.m, bmax);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_use);
+    float psum = 0.f;
+#pragma unroll
+    for (int t = 0; t < NQT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[t][r] = __builtin_amdgcn_exp2f(s[t][r] - m_use);
+        psum += p[t][r];
+      }
+    st.l = st.l * alpha + psum;
+    st.m = m_new;
+#pragma unroll
+    for (int n = 0; n < NV; ++n) st.O[n] *= alpha;
+  }
+
+  // O += P.V over one sub-tile.  Tokens that are not attended may hold any
+  // bits (NaN): their V elements are zeroed first (bit masks, no branch).
+  static __device__ __forceinline__ void pv(VTile& T, const float (&p)[NQT][4], State& st, int32_t lo, int32_t L,
+                                            int kg) {
+    uint32_t vmask[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < TPG; ++e) {
+      const int32_t tok = T.tok0 + TPG * kg + e;
+      const bool valid = T.ok && tok >= lo && tok < L;
+      const uint32_t field = EB == 4 ? 0xffffffffu : (EB == 2 ? 0xffffu : 0xffu);
+      vmask[e / EPW] |= valid ? field << (8 * EB * (e % EPW)) : 0u;
+    }
 #pragma unroll
     for (int n = 0; n < NV; ++n) {
-      if constexpr (KV == KV_F32) {
-        if (!valid[0]) t.v[n].x = 0;
-        if (!valid[1]) t.v[n].y = 0;
-        if (!valid[2]) t.v[n].z = 0;
-        if (!valid[3]) t.v[n].w = 0;
-      } else if constexpr (KV == KV_F16 || KV == KV_BF16) {
-        const uint32_t m0 = (valid[0] ? 0xffffu : 0u) | (valid[1] ? 0xffff0000u : 0u);
-        const uint32_t m1 = (valid[2] ? 0xffffu : 0u) | (valid[3] ? 0xffff0000u : 0u);
-        t.v[n].x &= m0;
-        t.v[n].y &= m1;
-      } else {
-        const uint32_t m = (valid[0] ? 0xffu : 0u) | (valid[1] ? 0xff00u : 0u) |
-                           (valid[2] ? 0xff0000u : 0u) | (valid[3] ? 0xff000000u : 0u);
-        t.v[n] &= m;
-      }
+      T.v[n].x &= vmask[0];
+      T.v[n].y &= vmask[1];
+      T.v[n].z &= vmask[2];
+      T.v[n].w &= vmask[3];
     }
-  }
-
-  static __device__ __forceinline__ void pv(const Tile& t, const float (&p)[4], f32x4 (&O)[NV]) {
     if constexpr (KV == KV_F32) {
 #pragma unroll
       for (int n = 0; n < NV; ++n) {
-        const float vf[4] = {__uint_as_float(t.v[n].x), __uint_as_float(t.v[n].y),
-                             __uint_as_float(t.v[n].z), __uint_as_float(t.v[n].w)};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) O[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[u], p[u], O[n], 0, 0, 0);
+        st.O[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(T.v[n].x), p[0][0], st.O[n], 0, 0, 0);
+        st.O[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(T.v[n].y), p[0][1], st.O[n], 0, 0, 0);
+        st.O[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(T.v[n].z), p[0][2], st.O[n], 0, 0, 0);
+        st.O[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(T.v[n].w), p[0][3], st.O[n], 0, 0, 0);
       }
     } else if constexpr (KV == KV_F16) {
-      f16x4 ph;
+      f16x8 ph;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) ph[u] = (_Float16)p[u];
+      for (int e = 0; e < 8; ++e) ph[e] = (_Float16)p[e / 4][e % 4];
 #pragma unroll
-      for (int n = 0; n < NV; ++n) {
-        f16x4 a;
-        __builtin_memcpy(&a, &t.v[n], 8);
-        O[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, ph, O[n], 0, 0, 0);
-      }
+      for (int n = 0; n < NV; ++n)
+        st.O[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as8<f16x8>(T.v[n]), ph, st.O[n], 0, 0, 0);
     } else {
-      // p = hi + lo, both bf16 (hi = round(p), lo = round(p - hi))
-      const f32x2 p01 = {p[0], p[1]};
-      const f32x2 p23 = {p[2], p[3]};
-      const bf16x2 h01 = __builtin_convertvector(p01, bf16x2);
-      const bf16x2 h23 = __builtin_convertvector(p23, bf16x2);
-      const f32x2 r01 = p01 - __builtin_convertvector(h01, f32x2);
-      const f32x2 r23 = p23 - __builtin_convertvector(h23, f32x2);
-      const bf16x2 l01 = __builtin_convertvector(r01, bf16x2);
-      const bf16x2 l23 = __builtin_convertvector(r23, bf16x2);
-      s16x4 phi, plo;
-      __builtin_memcpy(&phi, &h01, 4);
-      __builtin_memcpy(reinterpret_cast<char*>(&phi) + 4, &h23, 4);
-      __builtin_memcpy(&plo, &l01, 4);
-      __builtin_memcpy(reinterpret_cast<char*>(&plo) + 4, &l23, 4);
+      // P = hi + lo, both bf16 (hi = round(p), lo = round(p - hi)): the rounding
+      // of P stays far below the fp32 accumulation error.
+      constexpr int NC = TPG / 8;  // 32-token MFMA chunks per sub-tile
+      bf16x8 phi[NC], plo[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        f32x8 pf;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[e] = p[(8 * c + e) / 4][(8 * c + e) % 4];
+        phi[c] = __builtin_convertvector(pf, bf16x8);
+        plo[c] = __builtin_convertvector(pf - __builtin_convertvector(phi[c], f32x8), bf16x8);
+      }
 #pragma unroll
       for (int n = 0; n < NV; ++n) {
-        s16x4 a;
         if constexpr (KV == KV_BF16) {
-          __builtin_memcpy(&a, &t.v[n], 8);
+          const bf16x8 a = as8<bf16x8>(T.v[n]);
+          st.O[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi[0], st.O[n], 0, 0, 0);
+          st.O[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo[0], st.O[n], 0, 0, 0);
         } else {
-          a = e4m3x4_to_bf16x4(t.v[n]);
+          const bf16x8 a0 = e4m3x8_to_bf16x8(T.v[n].x, T.v[n].y);
+          const bf16x8 a1 = e4m3x8_to_bf16x8(T.v[n].z, T.v[n].w);
+          st.O[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, phi[0], st.O[n], 0, 0, 0);
+          st.O[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, plo[0], st.O[n], 0, 0, 0);
+          st.O[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, phi[1], st.O[n], 0, 0, 0);
+          st.O[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, plo[1], st.O[n], 0, 0, 0);
         }
-        O[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, phi, O[n], 0, 0, 0);
-        O[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, plo, O[n], 0, 0, 0);
       }
     }
   }
 
-  // One (KV head g, sequence b) piece: logical blocks [first + j0, first + j1).
-  // full: the piece is the whole attended range -> write the final output;
-  // otherwise write the partial to workspace slot (w, which).
-  static __device__ void piece(const DecodeParams& P, int b, int g, int j0, int j1, bool full,
-                               int64_t w, int which) {
+  // One (KV head g, sequence b) piece: units [j0, j1) of its attended range.
+  // full: the piece is the whole range -> write the final output; otherwise
+  // write the partial (unnormalised o, max, sum) to workspace slot (w, which)
+  // for merge_kernel.
+  static __device__ void piece(const DecodeParams& P, int b, int g, int j0, int j1, bool full, int64_t w,
+                               int which) {
     const int lane = threadIdx.x & 63;
     const int i = lane & 15;
     const int kg = lane >> 4;
-    int32_t L, lo, first, nb;
-    seq_extent<BS>(P, b, &L, &lo, &first, &nb);
+    int32_t L, lo, first, nu;
+    seq_extent<BS, U>(P, b, &L, &lo, &first, &nu);
     L = uniform(L);
     lo = uniform(lo);
     first = uniform(first);
 
-    qop qo[STEPS];
+    qop qo[NQ];
     load_q(P, b, g, i, kg, qo);
 
-    f32x4 O[NV];
+    State st;
 #pragma unroll
-    for (int n = 0; n < NV; ++n) O[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m = -INFINITY;
-    float lsum = 0.f;
+    for (int n = 0; n < NV; ++n) st.O[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.m = -INFINITY;
+    st.l = 0.f;
 
+    // block-table entries of the piece, 64 at a time (one per lane), the next
+    // 64 loaded ahead
     const int32_t* trow = P.tables + (int64_t)b * P.max_blocks;
-    const int64_t tile_elems = (int64_t)D * BS;
-    for (int j = j0; j < j1; ++j) {
-      const int blk = first + j;
-      const int32_t pb = uniform(trow[blk]);
-      if (pb < 0 || pb >= P.num_blocks) continue;
-      const int64_t tile = ((int64_t)P.layer * P.num_blocks + pb) * P.hkv + g;
-      const uint8_t* kblk = P.kc + tile * tile_elems * EB;
-      const uint8_t* vblk = P.vc + tile * tile_elems * EB;
-#pragma unroll
-      for (int st = 0; st < SUB; ++st) {
-        const int32_t t0 = blk * BS + 16 * st;
-        if (t0 + 16 <= lo || t0 >= L) continue;
-        Tile t;
-        load_tile(t, kblk, vblk, st, i, kg);
-        const f32x4 S = qk(t, qo);
-        // Masking is branch-free: a branch between the QK MFMAs and the first
-        // read of S would leave the MFMA-to-VALU wait states to the branch
-        // target.
-        float s[4];
-        bool valid[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int32_t tok = t0 + 4 * kg + r;
-          valid[r] = tok >= lo && tok < L;
-          s[r] = valid[r] ? S[r] * P.scale_log2 : -INFINITY;
-        }
-        mask_v(t, valid);
-        float bmax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-        bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-        bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-        const float m_new = fmaxf(m, bmax);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m - m_use);
-        float p[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(s[r] - m_use);
-        lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-        m = m_new;
-        if (__any(alpha != 1.0f)) {
-#pragma unroll
-          for (int n = 0; n < NV; ++n) O[n] *= alpha;
-        }
-        pv(t, p, O);
-      }
-    }
-    const float ltot = lsum + __shfl_xor(lsum, 16);
-    const float lall = ltot + __shfl_xor(ltot, 32);
+    const int32_t nblk_seq = (L + BS - 1) / BS;
+    const int32_t tb0 = first + j0 * UB;
+    const int32_t tb1 = min(first + j1 * UB, nblk_seq);
+    auto chunk = [&](int c) -> int32_t {
+      const int32_t idx = tb0 + 64 * c + lane;
+      return idx < tb1 ? trow[idx] : -1;
+    };
+    int32_t tcur = chunk(0);
+    int32_t tnext = tb1 - tb0 > 64 ? chunk(1) : -1;
+    int cur = 0;
 
-    // channel scale of V (FP8) and the output position
+    auto where = [&](int s) -> Addr {
+      const int u = s / SPU;
+      const int sub = s % SPU;
+      const int rel = u * UB;
+      const int c = rel >> 6;
+      if (c != cur) {
+        tcur = tnext;
+        tnext = tb0 + 64 * (c + 1) < tb1 ? chunk(c + 1) : -1;
+        cur = c;
+      }
+      int32_t ids[UB];
+#pragma unroll
+      for (int k = 0; k < UB; ++k) ids[k] = __builtin_amdgcn_readlane(tcur, (rel & 63) + k);
+      return locate(P, g, ids, sub, (tb0 + rel) * BS + sub * TT, i, kg);
+    };
+
+    // Staggered pipeline over sub-tiles: the K loads of sub-tile s+1 are in
+    // flight while s is scored, its V loads while s is accumulated.
+    const int nsub = (j1 - j0) * SPU;
+    KTile K0, K1;
+    VTile V0, V1;
+    f32x4 S[NQT];
+    float p[NQT][4];
+    Addr a0 = where(0), a1;
+    load_k(K0, a0);
+    load_v(V0, a0);
+    // sched_barrier keeps the compiler from hoisting the next sub-tile's
+    // loads above the current one's math (that would hold three half-tiles
+    // at once and spill).
+    for (int s = 0; s < nsub; s += 2) {
+      const bool n1 = s + 1 < nsub;
+      if (n1) {
+        a1 = where(s + 1);
+        load_k(K1, a1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      qk(K0, qo, S);
+      softmax(V0, S, st, p, lo, L, P.scale_log2, kg);
+      __builtin_amdgcn_sched_barrier(0);
+      if (n1) load_v(V1, a1);
+      __builtin_amdgcn_sched_barrier(0);
+      pv(V0, p, st, lo, L, kg);
+      __builtin_amdgcn_sched_barrier(0);
+      if (!n1) break;
+      const bool n2 = s + 2 < nsub;
+      if (n2) {
+        a0 = where(s + 2);
+        load_k(K0, a0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      qk(K1, qo, S);
+      softmax(V1, S, st, p, lo, L, P.scale_log2, kg);
+      __builtin_amdgcn_sched_barrier(0);
+      if (n2) load_v(V0, a0);
+      __builtin_amdgcn_sched_barrier(0);
+      pv(V1, p, st, lo, L, kg);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    const float l1 = st.l + __shfl_xor(st.l, 16);
+    const float lall = l1 + __shfl_xor(l1, 32);
+
+    // FP8: the per-channel V scale, applied once to the output
     float vsc[NV][4];
 #pragma unroll
     for (int n = 0; n < NV; ++n)
@@ -572,60 +736,42 @@ struct Decoder {
         for (int r = 0; r < 4; ++r) vsc[n][r] = sc[r];
       }
     }
-    if (i >= P.group) return;
+    const int G = P.group;
     if (full) {
+      if (i >= G) return;
       const float inv = lall > 0.f ? 1.0f / lall : 0.f;
-      const int64_t row = ((int64_t)b * P.hq + (int64_t)g * P.group + i) * D;
+      const int64_t row = ((int64_t)b * P.hq + (int64_t)g * G + i) * D;
 #pragma unroll
       for (int n = 0; n < NV; ++n) {
-        float o[4];
+        f32x4 o;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = O[n][r] * inv * vsc[n][r];
-        const int64_t off = row + 16 * n + 4 * kg;
-        if (P.out_dtype == PKV_F32) {
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(P.out) + off) = f32x4{o[0], o[1], o[2], o[3]};
-        } else if (P.out_dtype == PKV_BF16) {
-          const uint2 pk = make_uint2(f32_to_bf16_bits_rne(o[0]) | (f32_to_bf16_bits_rne(o[1]) << 16),
-                                      f32_to_bf16_bits_rne(o[2]) | (f32_to_bf16_bits_rne(o[3]) << 16));
-          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(P.out) + off) = pk;
-        } else {
-          const uint2 pk = make_uint2(f32_to_f16_bits(o[0]) | (f32_to_f16_bits(o[1]) << 16),
-                                      f32_to_f16_bits(o[2]) | (f32_to_f16_bits(o[3]) << 16));
-          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(P.out) + off) = pk;
-        }
+        for (int r = 0; r < 4; ++r) o[r] = st.O[n][r] * inv * vsc[n][r];
+        store4(P, row + 16 * n + 4 * kg, o);
       }
-    } else {
-      const int64_t slot = (w * 2 + which) * P.group + i;
+      return;
+    }
+    if (i < G) {
+      const int64_t slot = (w * 2 + which) * G + i;
       float* wo = P.ws_o + slot * D;
 #pragma unroll
       for (int n = 0; n < NV; ++n) {
         f32x4 o;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = O[n][r] * vsc[n][r];
+        for (int r = 0; r < 4; ++r) o[r] = st.O[n][r] * vsc[n][r];
         *reinterpret_cast<f32x4*>(wo + 16 * n + 4 * kg) = o;
       }
-      if (kg == 0) *reinterpret_cast<f32x2*>(P.ws_ml + slot * 2) = f32x2{m, lall};
+      if (kg == 0) *reinterpret_cast<f32x2*>(P.ws_ml + slot * 2) = f32x2{st.m, lall};
     }
   }
 };
 
-template <int D>
-__device__ __forceinline__ void write_zero_rows(const DecodeParams& P, int b, int g, int lane) {
-  // G rows of D outputs for (b, g)
-  const int64_t row0 = ((int64_t)b * P.hq + (int64_t)g * P.group) * D;
-  const int64_t n = (int64_t)P.group * D;
-  for (int64_t e = lane; e < n; e += 64) {
-    if (P.out_dtype == PKV_F32) reinterpret_cast<float*>(P.out)[row0 + e] = 0.f;
-    else reinterpret_cast<uint16_t*>(P.out)[row0 + e] = 0;
-  }
-}
-
 template <int KV, int D, int BS>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeParams P) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(DecodeParams P) {
   typedef Decoder<KV, D, BS> Dec;
+  constexpr int U = Units<KV, BS>::U;
   extern __shared__ int32_t C[];
   const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
+  const int wid = uniform((int)(threadIdx.x >> 6));  // wave-uniform: keeps all work indices scalar
   int64_t wg = blockIdx.x;
   if (P.xcd_remap) wg = (wg % 8) * (gridDim.x / 8) + wg / 8;
   const int64_t w = wg * 4 + wid;
@@ -635,112 +781,130 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams P) {
     if (w >= (int64_t)P.hkv * P.batch) return;
     const int g = (int)(w / P.batch);
     const int b = (int)(w % P.batch);
-    int32_t L, lo, first, nb;
-    seq_extent<BS>(P, b, &L, &lo, &first, &nb);
-    if (nb == 0) {
+    int32_t L, lo, first, nu;
+    seq_extent<BS, U>(P, b, &L, &lo, &first, &nu);
+    if (nu == 0) {
       write_zero_rows<D>(P, b, g, lane);
       return;
     }
-    Dec::piece(P, b, g, 0, nb, true, 0, 0);
+    Dec::piece(P, b, g, 0, nu, true, 0, 0);
     return;
   }
 
-  scan_block_counts<BS>(P, C);
+  scan_units<BS, U>(P, C);
   const int64_t t_head = C[P.batch];
   const int64_t T = t_head * P.hkv;
-  const int64_t W = P.num_waves;
-  if (w >= W || T == 0) return;
-  const int64_t r0 = range_start(w, T, W);
-  const int64_t r1 = range_start(w + 1, T, W);
-  int64_t x = r0;
-  while (x < r1) {
-    const int g = (int)(x / t_head);
-    const int32_t r = (int32_t)(x % t_head);
-    // largest b with C[b] <= r; blocks of b are [C[b], C[b+1])
-    int lo_b = 0, hi_b = P.batch - 1;
-    while (lo_b < hi_b) {
-      const int mid = (lo_b + hi_b + 1) >> 1;
-      if (C[mid] <= r) lo_b = mid;
-      else hi_b = mid - 1;
+  // sequences with nothing to attend get zero rows
+  const int64_t nseg = (int64_t)P.hkv * P.batch;
+  const int64_t launched = (int64_t)gridDim.x * 4;
+  for (int64_t seg = w; seg < nseg; seg += launched) {
+    const int b = (int)(seg % P.batch);
+    if (C[b + 1] == C[b]) {
+      write_zero_rows<D>(P, b, (int)(seg / P.batch), lane);
+      if (lane == 0) P.ws_job[seg] = make_int4(0, 0, 0, 0);
     }
-    const int b = uniform(lo_b);
-    const int32_t cb = uniform(C[b]);
-    const int32_t nb = uniform(C[b + 1]) - cb;
-    const int32_t j0 = r - cb;
-    const int64_t seg_end = x - j0 + nb;
-    const int64_t pend = seg_end < r1 ? seg_end : r1;
-    const int32_t j1 = j0 + (int32_t)(pend - x);
-    const bool full = j0 == 0 && j1 == nb;
-    Dec::piece(P, b, g, j0, j1, full, w, x == r0 ? 0 : 1);
-    x = pend;
+  }
+  if (w >= P.num_waves) return;
+  // all units of all (KV head, sequence) pairs laid end to end, KV-head
+  // major, cut into W equal non-empty ranges
+  const int64_t W = P.num_waves < T ? P.num_waves : T;
+  if (w < W) {
+    const int64_t r0 = range_start(w, T, W);
+    const int64_t r1 = range_start(w + 1, T, W);
+    int64_t x = r0;
+    while (x < r1) {
+      const int g = (int)(x / t_head);
+      const int32_t r = (int32_t)(x % t_head);
+      // largest b with C[b] <= r; the units of b are [C[b], C[b+1])
+      int lo_b = 0, hi_b = P.batch - 1;
+      while (lo_b < hi_b) {
+        const int mid = (lo_b + hi_b + 1) >> 1;
+        if (C[mid] <= r) lo_b = mid;
+        else hi_b = mid - 1;
+      }
+      const int b = uniform(lo_b);
+      const int32_t cb = uniform(C[b]);
+      const int32_t nb = uniform(C[b + 1]) - cb;
+      const int32_t j0 = r - cb;
+      const int64_t seg_start = x - j0;
+      const int64_t seg_end = seg_start + nb;
+      const int64_t pend = seg_end < r1 ? seg_end : r1;
+      const int32_t j1 = j0 + (int32_t)(pend - x);
+      const bool full = j0 == 0 && j1 == nb;
+      const int which = x == r0 ? 0 : 1;
+      Dec::piece(P, b, g, j0, j1, full, w, which);
+      // the range holding a sequence's first piece writes its merge job
+      if (j0 == 0 && lane == 0)
+        P.ws_job[(int64_t)g * P.batch + b] =
+            full ? make_int4(0, 0, 0, 0) : make_int4((int)w, (int)(wave_of(seg_end - 1, T, W) - w + 1), which, 0);
+      x = pend;
+    }
   }
 }
 
-// One wavefront per (KV head, sequence): zero an empty sequence, or combine
-// the pieces of a sequence whose blocks straddle wavefront ranges.
-template <int D, int BS>
-__global__ __launch_bounds__(256) void merge_kernel(DecodeParams P) {
-  extern __shared__ int32_t C[];
-  scan_block_counts<BS>(P, C);
-  const int lane = threadIdx.x & 63;
-  const int64_t seg = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (seg >= (int64_t)P.hkv * P.batch) return;
-  const int g = (int)(seg / P.batch);
-  const int b = (int)(seg % P.batch);
-  const int32_t nb = C[b + 1] - C[b];
-  if (nb == 0) {
-    write_zero_rows<D>(P, b, g, lane);
-    return;
-  }
-  const int64_t t_head = C[P.batch];
-  const int64_t T = t_head * P.hkv;
-  const int64_t W = P.num_waves;
-  const int64_t s0 = (int64_t)g * t_head + C[b];
-  const int64_t s1 = s0 + nb;
-  const int64_t wf = wave_of(s0, T, W);
-  const int64_t wl = wave_of(s1 - 1, T, W);
-  if (wf == wl) return;  // whole sequence inside one range: already final
-  const int first_which = s0 == range_start(wf, T, W) ? 0 : 1;
-  constexpr int LPH = D / 4;      // lanes per head row
-  constexpr int HPI = 64 / LPH;   // heads per iteration
-  const int hl = lane / LPH;
-  const int d4 = (lane % LPH) * 4;
-  for (int h0 = 0; h0 < P.group; h0 += HPI) {
-    const int h = h0 + hl;
-    if (h >= P.group) continue;
-    // wavefronts with an empty range (more wavefronts than blocks) hold no piece
-    float M = -INFINITY;
-    for (int64_t wv = wf; wv <= wl; ++wv) {
-      if (range_start(wv + 1, T, W) == range_start(wv, T, W)) continue;
-      const int which = wv == wf ? first_which : 0;
-      M = fmaxf(M, P.ws_ml[((wv * 2 + which) * P.group + h) * 2]);
-    }
+// Log-sum-exp merge of the pieces of one (KV head, sequence) per workgroup:
+// thread (position, sub) merges pieces sub, sub + TPP, ... of output position
+// (head h, 4 dims), where TPP threads share a position; the TPP partial merges
+// are combined with lane exchanges in a fixed order (deterministic).  Piece p
+// of a job whose first piece is in range w0 is in slot (w0, first) for p = 0
+// and (w0 + p, 0) after.
+template <int D>
+__global__ __launch_bounds__(1024) void merge_kernel(DecodeParams P) {
+  const int64_t seg = blockIdx.x;
+  const int4 job = P.ws_job[seg];
+  const int npieces = job.y;
+  if (npieces == 0) return;
+  const int64_t w = job.x;
+  const int first_which = job.z;
+  const int b = (int)(seg % P.batch), g = (int)(seg / P.batch);
+  constexpr int D4 = D / 4;
+  const int G = P.group;
+  const int NP = G * D4;
+  const int nthr = blockDim.x;
+  int tpp = 1;
+  while (tpp * 2 * NP <= nthr && tpp < 16) tpp *= 2;   // threads per position (lanes of one wavefront)
+  const int tid = threadIdx.x;
+  const int sub = tid % tpp;
+  for (int pos = tid / tpp; pos < NP; pos += nthr / tpp) {
+    const int h = pos / D4;
+    const int d4 = (pos % D4) * 4;
+    float M = -INFINITY, Ls = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float Lsum = 0.f;
-    if (M != -INFINITY) {
-      for (int64_t wv = wf; wv <= wl; ++wv) {
-        if (range_start(wv + 1, T, W) == range_start(wv, T, W)) continue;
-        const int which = wv == wf ? first_which : 0;
-        const int64_t slot = (wv * 2 + which) * P.group + h;
-        const f32x2 ml = *reinterpret_cast<const f32x2*>(P.ws_ml + slot * 2);
-        const float wt = __builtin_amdgcn_exp2f(ml[0] - M);
-        Lsum += wt * ml[1];
-        acc += wt * *reinterpret_cast<const f32x4*>(P.ws_o + slot * D + d4);
-      }
+#pragma unroll 8
+    for (int p = sub; p < npieces; p += tpp) {
+      const int64_t wv = w + p;
+      const int64_t slot = (wv * 2 + (p == 0 ? first_which : 0)) * G + h;
+      const f32x2 ml = *reinterpret_cast<const f32x2*>(P.ws_ml + slot * 2);
+      const f32x4 o = *reinterpret_cast<const f32x4*>(P.ws_o + slot * D + d4);
+      const float Mn = fmaxf(M, ml[0]);
+      const float Mu = Mn == -INFINITY ? 0.f : Mn;
+      const float a = __builtin_amdgcn_exp2f(M - Mu);
+      const float wt = __builtin_amdgcn_exp2f(ml[0] - Mu);
+      acc = acc * a + o * wt;
+      Ls = Ls * a + ml[1] * wt;
+      M = Mn;
     }
-    const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
-    const int64_t off = ((int64_t)b * P.hq + (int64_t)g * P.group + h) * D + d4;
-    const f32x4 o = acc * inv;
-    if (P.out_dtype == PKV_F32) {
-      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(P.out) + off) = o;
-    } else if (P.out_dtype == PKV_BF16) {
-      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(P.out) + off) =
-          make_uint2(f32_to_bf16_bits_rne(o[0]) | (f32_to_bf16_bits_rne(o[1]) << 16),
-                     f32_to_bf16_bits_rne(o[2]) | (f32_to_bf16_bits_rne(o[3]) << 16));
-    } else {
-      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(P.out) + off) =
-          make_uint2(f32_to_f16_bits(o[0]) | (f32_to_f16_bits(o[1]) << 16),
-                     f32_to_f16_bits(o[2]) | (f32_to_f16_bits(o[3]) << 16));
+    for (int off = 1; off < tpp; off <<= 1) {
+      const float Mo = __shfl_xor(M, off);
+      const float Lo = __shfl_xor(Ls, off);
+      f32x4 ao;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) ao[c] = __shfl_xor(acc[c], off);
+      // combine in a fixed order: lower sub first
+      const bool lower = (sub & off) == 0;
+      const float M1 = lower ? M : Mo, M2 = lower ? Mo : M;
+      const float L1 = lower ? Ls : Lo, L2 = lower ? Lo : Ls;
+      const f32x4 A1 = lower ? acc : ao, A2 = lower ? ao : acc;
+      const float Mn = fmaxf(M1, M2);
+      const float Mu = Mn == -INFINITY ? 0.f : Mn;
+      const float e1 = __builtin_amdgcn_exp2f(M1 - Mu), e2 = __builtin_amdgcn_exp2f(M2 - Mu);
+      acc = A1 * e1 + A2 * e2;
+      Ls = L1 * e1 + L2 * e2;
+      M = Mn;
+    }
+    if (sub == 0) {
+      const float inv = Ls > 0.f ? 1.0f / Ls : 0.f;
+      store4(P, ((int64_t)b * P.hq + (int64_t)g * G + h) * D + d4, acc * inv);
     }
   }
 }
@@ -748,7 +912,8 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams P) {
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-static constexpr int kWavesPerCU = 8;
+static constexpr int kWavesPerCU = 4;
+static constexpr int64_t kMaxWaves = 16384;   // largest split count
 static constexpr int kMaxBatch = 16000;   // C[] of B+1 ints in LDS
 
 static pkv_status hip_fail(hipError_t e, const char* what) {
@@ -793,6 +958,7 @@ static pkv_status check_decode(const kv_pool* pool, const paged_decode_args* a) 
   if (a->num_q_heads / d.num_kv_heads > 16) return fail(PKV_E_UNSUPPORTED, "query group above 16");
   if (a->max_blocks_per_seq < 0 || a->sliding_window < 0 || a->num_splits < 0)
     return fail(PKV_E_INVAL, "negative max_blocks_per_seq, sliding_window or num_splits");
+  if (a->num_splits > kMaxWaves) return fail(PKV_E_UNSUPPORTED, "num_splits above 16384");
   if (a->q_dtype != expected_q_dtype(d.kv_dtype))
     return fail(PKV_E_DTYPE, "q_dtype must be f32 / f16 / bf16 for f32 / f16 / (bf16, fp8) pools");
   if (a->out_dtype != PKV_F32 && a->out_dtype != PKV_F16 && a->out_dtype != PKV_BF16)
@@ -800,6 +966,8 @@ static pkv_status check_decode(const kv_pool* pool, const paged_decode_args* a) 
   if (!std::isfinite(a->scale)) return fail(PKV_E_INVAL, "scale must be finite");
   if (a->batch > 0 && (!a->q || !a->out || !a->context_lens || (a->max_blocks_per_seq > 0 && !a->block_tables)))
     return fail(PKV_E_INVAL, "null device pointer");
+  if ((reinterpret_cast<uintptr_t>(a->q) | reinterpret_cast<uintptr_t>(a->out)) % 16)
+    return fail(PKV_E_INVAL, "q and out must be 16-byte aligned");
   return PKV_OK;
 }
 
@@ -807,11 +975,23 @@ static int64_t num_waves_for(const paged_decode_args* a, int cus) {
   return a->num_splits >= 2 ? (int64_t)a->num_splits : (int64_t)cus * kWavesPerCU;
 }
 
-static size_t workspace_for(const kv_pool* pool, const paged_decode_args* a, int64_t W) {
+// Workspace: merge jobs [Hkv][B] int4, partial outputs [W][2][G][D] fp32
+// and partial (max, sum) [W][2][G][2] fp32, each part 256-byte aligned.
+// Every call writes each job record before merge_kernel reads it, so the
+// workspace needs no initialisation.
+struct WsLayout {
+  size_t job_off, o_off, ml_off, total;
+};
+
+static WsLayout workspace_layout(const kv_pool* pool, const paged_decode_args* a, int64_t W) {
   const int64_t G = a->num_q_heads / pool->desc.num_kv_heads;
-  const size_t o = (size_t)W * 2 * G * pool->desc.head_dim * sizeof(float);
-  const size_t ml = (size_t)W * 2 * G * 2 * sizeof(float);
-  return ((o + 255) / 256) * 256 + ml;
+  auto up = [](size_t x) { return ((x + 255) / 256) * 256; };
+  WsLayout l;
+  l.job_off = 0;
+  l.o_off = up((size_t)pool->desc.num_kv_heads * a->batch * sizeof(int4));
+  l.ml_off = l.o_off + up((size_t)W * 2 * G * pool->desc.head_dim * sizeof(float));
+  l.total = l.ml_off + up((size_t)W * 2 * G * 2 * sizeof(float));
+  return l;
 }
 
 typedef void (*decode_fn)(DecodeParams);
@@ -841,19 +1021,6 @@ static decode_fn pick_decode(int kv, int d, int bs) {
   }
   return nullptr;
 }
-
-template <int D>
-static decode_fn pick_merge_bs(int bs) {
-  switch (bs) {
-    case 16: return merge_kernel<D, 16>;
-    case 32: return merge_kernel<D, 32>;
-    case 64: return merge_kernel<D, 64>;
-    case 128: return merge_kernel<D, 128>;
-  }
-  return nullptr;
-}
-
-static decode_fn pick_merge(int d, int bs) { return d == 64 ? pick_merge_bs<64>(bs) : pick_merge_bs<128>(bs); }
 
 }  // namespace pkv
 
@@ -943,7 +1110,7 @@ pkv_status paged_attention_workspace_size(const kv_pool* pool, const paged_decod
     st = device_cus(&cus);
     if (st != PKV_OK) return st;
   }
-  *bytes_out = workspace_for(pool, a, num_waves_for(a, cus));
+  *bytes_out = workspace_layout(pool, a, num_waves_for(a, cus)).total;
   return PKV_OK;
 }
 
@@ -973,6 +1140,7 @@ pkv_status paged_attention_decode(const kv_pool* pool, const paged_decode_args* 
   P.scale_log2 = a->scale * 1.4426950408889634f;
   P.ws_o = nullptr;
   P.ws_ml = nullptr;
+  P.ws_job = nullptr;
   P.xcd_remap = 0;
   decode_fn fn = pick_decode(d.kv_dtype, d.head_dim, d.block_size);
   if (!fn) return fail(PKV_E_UNSUPPORTED, "no kernel for this shape");
@@ -994,26 +1162,28 @@ pkv_status paged_attention_decode(const kv_pool* pool, const paged_decode_args* 
     if (st != PKV_OK) return st;
   }
   const int64_t W = num_waves_for(a, cus);
-  if (W > INT32_MAX / 2) return fail(PKV_E_INVAL, "num_splits too large");
-  const size_t need = workspace_for(pool, a, W);
-  if (!a->workspace || a->workspace_bytes < need)
+  const WsLayout wl = workspace_layout(pool, a, W);
+  if (!a->workspace || a->workspace_bytes < wl.total)
     return fail(PKV_E_INVAL, "workspace missing or smaller than paged_attention_workspace_size()");
   if (reinterpret_cast<uintptr_t>(a->workspace) % 256) return fail(PKV_E_INVAL, "workspace must be 256-byte aligned");
-  const int64_t G = P.group;
-  P.ws_o = reinterpret_cast<float*>(a->workspace);
-  const size_t o_bytes = (size_t)W * 2 * G * d.head_dim * sizeof(float);
-  P.ws_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(a->workspace) + ((o_bytes + 255) / 256) * 256);
+  char* ws = reinterpret_cast<char*>(a->workspace);
+  P.ws_o = reinterpret_cast<float*>(ws + wl.o_off);
+  P.ws_ml = reinterpret_cast<float*>(ws + wl.ml_off);
+  P.ws_job = reinterpret_cast<int4*>(ws + wl.job_off);
   P.single = 0;
   P.num_waves = (int32_t)W;
-  const int64_t grid = (W + 3) / 4;
-  P.xcd_remap = grid % 8 == 0 ? 1 : 0;
+  int64_t grid = (W + 3) / 4;
+  grid = ((grid + 7) / 8) * 8;  // whole rounds over the 8 XCDs
+  P.xcd_remap = 1;
   const size_t lds = (size_t)(a->batch + 1) * sizeof(int32_t);
   hipLaunchKernelGGL(fn, dim3((uint32_t)grid), dim3(256), lds, s, P);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "decode launch");
-  decode_fn mfn = pick_merge(d.head_dim, d.block_size);
-  const int64_t mgrid = (segs + 3) / 4;
-  hipLaunchKernelGGL(mfn, dim3((uint32_t)mgrid), dim3(256), lds, s, P);
+  // few sequences: wide workgroups (many pieces each); many: narrow ones, so
+  // that the dispatch of workgroups with nothing to merge stays cheap
+  const int mthreads = segs <= 512 ? 1024 : 256;
+  hipLaunchKernelGGL(d.head_dim == 64 ? merge_kernel<64> : merge_kernel<128>, dim3((uint32_t)segs),
+                     dim3(mthreads), 0, s, P);
   e = hipGetLastError();
   return e == hipSuccess ? PKV_OK : hip_fail(e, "merge launch");
 }

@@ -286,6 +286,59 @@ pkv_status block_table_free(kv_pool* p, int32_t seq) {
   PKV_GUARD_END
 }
 
+pkv_status block_table_fork_batch(kv_pool* p, const int32_t* parents, int32_t n, int32_t* children_out) {
+  PKV_GUARD_BEGIN
+  if (!p || n < 0 || (n > 0 && (!parents || !children_out))) return fail(PKV_E_INVAL, "bad argument");
+  if ((int64_t)p->next_id + n > (int64_t)INT32_MAX) return fail(PKV_E_INVAL, "sequence ids exhausted");
+  // copy every parent first (may throw: nothing changed yet)
+  std::vector<Sequence> copies;
+  copies.reserve(n);
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = p->seqs.find(parents[i]);
+    if (it == p->seqs.end()) return fail(PKV_E_INVAL, "unknown sequence id in batch");
+    copies.push_back(it->second);
+  }
+  const int32_t id0 = p->next_id;
+  int32_t done = 0;
+  try {
+    p->seqs.reserve(p->seqs.size() + n);
+    for (; done < n; ++done) p->seqs.emplace(id0 + done, std::move(copies[done]));
+  } catch (...) {
+    for (int32_t i = 0; i < done; ++i) p->seqs.erase(id0 + i);
+    throw;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    for (int32_t b : p->seqs.find(id0 + i)->second.table) p->refcount[b] += 1;
+    children_out[i] = id0 + i;
+  }
+  p->next_id += n;
+  return PKV_OK;
+  PKV_GUARD_END
+}
+
+pkv_status block_table_free_batch(kv_pool* p, const int32_t* seqs, int32_t n) {
+  PKV_GUARD_BEGIN
+  if (!p || n < 0 || (n > 0 && !seqs)) return fail(PKV_E_INVAL, "bad argument");
+  std::vector<std::unordered_map<int32_t, Sequence>::iterator> its;
+  its.reserve(n);
+  std::unordered_map<int32_t, char> seen;
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = p->seqs.find(seqs[i]);
+    if (it == p->seqs.end()) return fail(PKV_E_INVAL, "unknown sequence id in batch");
+    if (!seen.emplace(seqs[i], 1).second) return fail(PKV_E_INVAL, "duplicate sequence in batch");
+    its.push_back(it);
+  }
+  for (auto it : its) {
+    for (int32_t b : it->second.table) {
+      p->refcount[b] -= 1;
+      if (p->refcount[b] == 0) push_free(p, b);
+    }
+    p->seqs.erase(it);
+  }
+  return PKV_OK;
+  PKV_GUARD_END
+}
+
 pkv_status block_table_get(const kv_pool* p, int32_t seq, int32_t* blocks_out, int32_t cap,
                            int32_t* n_blocks_out, int32_t* len_out) {
   if (!p || !n_blocks_out || !len_out || cap < 0 || (cap > 0 && !blocks_out))

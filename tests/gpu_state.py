@@ -93,7 +93,7 @@ class GpuState:
         a = P.make_decode_args(layer, B, w.num_q_heads, tables.shape[1], qd, w.q_dtype, td, ld, scale,
                                out, out_dtype, sliding_window=window, num_splits=num_splits)
         ws_bytes = P.paged_attention_workspace_size(self.pool.handle, a)
-        ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
         a.workspace, a.workspace_bytes = ws.data_ptr(), ws_bytes
         P.paged_attention_decode(self.pool.handle, a)
         torch.cuda.synchronize()

@@ -73,16 +73,30 @@ def test_block_manager_matches_oracle(seed):
                 c, o = P.block_table_alloc(h), bm.alloc()
                 assert c == o
                 ids[c] = o
-            elif op < 0.25:
+            elif op < 0.2:
                 p = rng.choice(live)
                 c, o = P.block_table_fork(h, p), bm.fork(ids[p])
                 assert c == o
                 ids[c] = o
-            elif op < 0.35:
+            elif op < 0.25:
+                # batch fork: the same as forking each parent in order
+                parents = [rng.choice(live) for _ in range(rng.randint(1, 4))]
+                kids = P.block_table_fork_batch(h, parents).tolist()
+                okids = [bm.fork(ids[p]) for p in parents]
+                assert kids == okids
+                ids.update(zip(kids, okids))
+            elif op < 0.32:
                 s = rng.choice(live)
                 P.block_table_free(h, s)
                 bm.free(ids[s])
                 del ids[s]
+            elif op < 0.35:
+                # batch free: the same as freeing each sequence in order
+                batch = rng.sample(live, rng.randint(1, len(live)))
+                P.block_table_free_batch(h, batch)
+                for s in batch:
+                    bm.free(ids[s])
+                    del ids[s]
             elif op < 0.6:
                 batch = rng.sample(live, rng.randint(1, len(live)))
                 try:
@@ -147,6 +161,17 @@ def test_errors_and_strong_guarantee():
             P.block_table_append(h, s, -1)
         with pytest.raises(P.PagedKVError):
             P.block_table_append_batch(h, [s, s])
+        # batch fork / free are all or nothing
+        before = (P.kv_pool_free_list(h), P.block_table_get(h, s), P.kv_pool_refcount(h, 0))
+        with pytest.raises(P.PagedKVError):
+            P.block_table_fork_batch(h, [s, 99])
+        with pytest.raises(P.PagedKVError):
+            P.block_table_free_batch(h, [s, s])
+        with pytest.raises(P.PagedKVError):
+            P.block_table_free_batch(h, [s, 99])
+        assert (P.kv_pool_free_list(h), P.block_table_get(h, s), P.kv_pool_refcount(h, 0)) == before
+        assert P.block_table_alloc(h) == s + 1     # the failed fork took no id
+        P.block_table_free(h, s + 1)
         with pytest.raises(P.PagedKVError):
             P.block_table_export(h, [s], 2)
         with pytest.raises(P.PagedKVError):
@@ -193,7 +218,7 @@ def test_decode_argument_validation_on_host():
                     block_tables=2048, context_lens=4096, scale=0.1, out=8192)
         cases = [dict(layer=1), dict(num_q_heads=3), dict(num_q_heads=34), dict(q_dtype="f16"),
                  dict(out_dtype="fp8"), dict(scale=float("nan")), dict(batch=-1),
-                 dict(sliding_window=-1), dict(q=None)]
+                 dict(sliding_window=-1), dict(q=None), dict(q=1032), dict(out=8200)]
         for c in cases:
             kw = dict(base)
             kw.update(c)
@@ -202,7 +227,7 @@ def test_decode_argument_validation_on_host():
         # explicit split count: the workspace size needs no device
         a = P.make_decode_args(**base, num_splits=10)
         ws = P.paged_attention_workspace_size(h, a)
-        assert ws >= 10 * 2 * 2 * (128 + 2) * 4
+        assert ws >= 10 * 2 * 2 * (128 + 2) * 4 + 2 * 1 * 4   # partials + counters
         # single pass needs none
         a1 = P.make_decode_args(**base, num_splits=1)
         assert P.paged_attention_workspace_size(h, a1) == 0

@@ -255,3 +255,34 @@ def test_fp8_encoder_bit_exact():
         assert np.array_equal(k[blk, 0, off], want[t, 0]), t
         assert np.array_equal(v[blk, 0, off], want[t, 0]), t
     pool.close()
+
+
+def test_workspace_reused_across_calls():
+    # One workspace, never initialised (filled with 0xFF bytes), serves many
+    # calls with different batch sizes and split counts; the results stay
+    # bitwise identical to calls with a fresh workspace each.
+    w, d, ost, gst = _state("gqa8_bf16")
+    tables, lens = ost.export()
+    q = wl.q_bits(w)
+    ref = _oracle_out(ost, q, tables, lens)
+    splits = (0, 7, 64, 2)
+    fresh = {s: gst.decode(q, tables, lens, num_splits=s) for s in splits}
+    nbytes = 0
+    for s in splits:
+        a = P.make_decode_args(0, w.batch, w.num_q_heads, tables.shape[1], 16, w.q_dtype, 16, 16, 0.1, 16,
+                               num_splits=s)
+        nbytes = max(nbytes, P.paged_attention_workspace_size(gst.pool.handle, a))
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
+    qd, td, ld = to_dev(q), torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda()
+    scale = 1.0 / math.sqrt(w.head_dim)
+    for rep in range(2):
+        for s, B in ((0, w.batch), (7, w.batch), (64, 4), (2, w.batch), (0, 3), (7, 6)):
+            out = torch.full((B, w.num_q_heads, w.head_dim), -7.0, dtype=torch.float32, device="cuda")
+            a = P.make_decode_args(0, B, w.num_q_heads, tables.shape[1], qd, w.q_dtype, td, ld, scale, out,
+                                   num_splits=s, workspace=ws, workspace_bytes=nbytes)
+            P.paged_attention_decode(gst.pool.handle, a)
+            torch.cuda.synchronize()
+            got = out.cpu().numpy().astype(np.float64)
+            if B == w.batch:
+                assert np.array_equal(got, fresh[s]), (rep, s, B)
+            assert np.abs(got - ref[:B]).max() <= TOL[w.kv_dtype], (rep, s, B)
