@@ -49,6 +49,23 @@ WORKLOAD_NAMES = {
 }
 
 
+# HBM bytes per paged_attention_decode call (decode_kernel + merge_kernel, read +
+# write), from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs scaled by what the
+# same counters read for a plain 1 GiB device copy (FETCH x 2.0, WRITE x 1.0).
+# Each entry holds for the kernel source it was measured on (sha256 prefix of
+# csrc/kernels.hip); for any other source the figure is not reported.
+MEASURED_TRAFFIC = {
+    "c3": (517.6e6, "9325eaef9d821ebe"),
+}
+
+
+def kernels_sha():
+    import hashlib
+    path = os.path.join(ROOT, "paged_kv_cache_406_amd", "csrc", "kernels.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
 def log(msg):
     sys.stderr.write(f"[bench] {msg}\n")
     sys.stderr.flush()
@@ -279,6 +296,9 @@ def run(args):
     log(f"step {step_ms:.4f} ms (host wall {1e3 * wall / args.steps:.4f} ms), decode {avg_dec_ms:.4f} ms "
         f"(min {min(dec_ms):.4f}, max {max(dec_ms):.4f})")
     value = avg_bytes / (step_ms * 1e-3) / 1e9
+    traffic = args.traffic * 1e9 if args.traffic else None
+    if traffic is None and w.name in MEASURED_TRAFFIC and MEASURED_TRAFFIC[w.name][1] == kernels_sha():
+        traffic = MEASURED_TRAFFIC[w.name][0]
     achieved = avg_bytes / (avg_dec_ms * 1e-3) / 1e9
     res = {
         "metric": METRIC,
@@ -311,8 +331,8 @@ def run(args):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": args.traffic,
-            "kernel": "paged_attention_decode (decode_kernel, log-sum-exp merge inside)",
+            "traffic": traffic,
+            "kernel": "paged_attention_decode (decode_kernel + merge_kernel)",
         },
         "cpu_baseline": None,
     }
@@ -371,6 +391,19 @@ def cpu_baseline(w, d, budget_s):
     }
 
 
+def copy_probe(nbytes, reps):
+    """A plain device-to-device copy of known size, run under rocprofv3 --pmc
+    so that FETCH_SIZE / WRITE_SIZE can be calibrated against bytes moved."""
+    import torch
+    torch.cuda.set_device(0)
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -383,7 +416,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", type=float, default=None,
                     help="HBM bytes per decode call from rocprofv3 counters (GB)")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="only run a plain device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
+    if args.copy_probe:
+        copy_probe(args.copy_probe, 5)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the decode path runs on a single MI355X; "
               "multi-GPU runs are not part of this benchmark", file=sys.stderr)

@@ -285,6 +285,10 @@ def make_decode_args(layer, batch, num_q_heads, max_blocks_per_seq, q, q_dtype, 
     a.scale = scale
     a.out, a.out_dtype = _ptr(out), DTYPE_CODE.get(out_dtype, out_dtype)
     a.workspace, a.workspace_bytes = _ptr(workspace), workspace_bytes
+    # the struct holds raw device addresses: keep the tensors they came from
+    # alive as long as the struct, or torch may hand their memory to the next
+    # allocation before the decode is launched
+    a._refs = (q, block_tables, context_lens, out, workspace)
     return a
 
 

@@ -260,3 +260,22 @@ def test_one_hip_runtime_in_process():
     res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
     assert res.returncode == 0, res.stderr
     assert res.stdout.strip() == "1", res.stdout
+
+
+def test_decode_args_keep_their_tensors_alive():
+    # the args struct stores raw addresses; the tensors behind them must live
+    # as long as the struct (else torch may reuse their memory before launch)
+    import gc
+    import weakref
+    import torch
+    q = torch.zeros(4, 8)
+    tables = torch.zeros(4, 2, dtype=torch.int32)
+    a = P.make_decode_args(0, 4, 8, 2, q, "f32", tables, torch.zeros(4, dtype=torch.int32), 0.1,
+                           torch.zeros(4, 8))
+    refs = [weakref.ref(t) for t in a._refs if t is not None]
+    del q, tables
+    gc.collect()
+    assert len(refs) == 4 and all(r() is not None for r in refs)
+    del a
+    gc.collect()
+    assert all(r() is None for r in refs)
