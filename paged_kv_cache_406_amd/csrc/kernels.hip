@@ -842,65 +842,57 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   }
 }
 
-// Log-sum-exp merge of the pieces of one (KV head, sequence) per workgroup:
-// thread (position, sub) merges pieces sub, sub + TPP, ... of output position
-// (head h, 4 dims), where TPP threads share a position; the TPP partial merges
-// are combined with lane exchanges in a fixed order (deterministic).  Piece p
-// of a job whose first piece is in range w0 is in slot (w0, first) for p = 0
-// and (w0 + p, 0) after.
+// Log-sum-exp merge of the pieces of a split (KV head, sequence).  Workgroup
+// (seg, y) of 256 threads owns a contiguous share of the G * D/4 output
+// positions (head h, 4 dims) of sequence-head seg; TPP threads share a
+// position, thread sub taking pieces sub, sub + TPP, ...  Two passes with no
+// dependent chain: the max of the piece maxima (exact, order-free), then the
+// rescaled sums.  Lane-exchange butterflies leave the same bits in every lane
+// of a position (deterministic).  Piece p of a job whose first piece is in
+// range w0 is in slot (w0, first) for p = 0 and (w0 + p, 0) after.
 template <int D>
-__global__ __launch_bounds__(1024) void merge_kernel(DecodeParams P) {
+__global__ __launch_bounds__(256) void merge_kernel(DecodeParams P) {
   const int64_t seg = blockIdx.x;
   const int4 job = P.ws_job[seg];
   const int npieces = job.y;
   if (npieces == 0) return;
-  const int64_t w = job.x;
+  const int64_t w0 = job.x;
   const int first_which = job.z;
   const int b = (int)(seg % P.batch), g = (int)(seg / P.batch);
   constexpr int D4 = D / 4;
   const int G = P.group;
   const int NP = G * D4;
-  const int nthr = blockDim.x;
+  const int npg = (NP + gridDim.y - 1) / gridDim.y;
+  const int pos0 = blockIdx.y * npg;
+  const int pos1 = min(NP, pos0 + npg);
   int tpp = 1;
-  while (tpp * 2 * NP <= nthr && tpp < 16) tpp *= 2;   // threads per position (lanes of one wavefront)
+  while (tpp * 2 * npg <= 256 && tpp < 64) tpp *= 2;   // threads per position (lanes of one wavefront)
   const int tid = threadIdx.x;
   const int sub = tid % tpp;
-  for (int pos = tid / tpp; pos < NP; pos += nthr / tpp) {
+  for (int pos = pos0 + tid / tpp; pos < pos1; pos += 256 / tpp) {
     const int h = pos / D4;
     const int d4 = (pos % D4) * 4;
-    float M = -INFINITY, Ls = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    auto slot = [&](int pc) -> int64_t { return ((w0 + pc) * 2 + (pc == 0 ? first_which : 0)) * G + h; };
+    float M = -INFINITY;
 #pragma unroll 8
-    for (int p = sub; p < npieces; p += tpp) {
-      const int64_t wv = w + p;
-      const int64_t slot = (wv * 2 + (p == 0 ? first_which : 0)) * G + h;
-      const f32x2 ml = *reinterpret_cast<const f32x2*>(P.ws_ml + slot * 2);
-      const f32x4 o = *reinterpret_cast<const f32x4*>(P.ws_o + slot * D + d4);
-      const float Mn = fmaxf(M, ml[0]);
-      const float Mu = Mn == -INFINITY ? 0.f : Mn;
-      const float a = __builtin_amdgcn_exp2f(M - Mu);
+    for (int pc = sub; pc < npieces; pc += tpp) M = fmaxf(M, P.ws_ml[slot(pc) * 2]);
+    for (int off = 1; off < tpp; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+    const float Mu = M == -INFINITY ? 0.f : M;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float Ls = 0.f;
+#pragma unroll 8
+    for (int pc = sub; pc < npieces; pc += tpp) {
+      const int64_t sl = slot(pc);
+      const f32x2 ml = *reinterpret_cast<const f32x2*>(P.ws_ml + sl * 2);
+      const f32x4 o = *reinterpret_cast<const f32x4*>(P.ws_o + sl * D + d4);
       const float wt = __builtin_amdgcn_exp2f(ml[0] - Mu);
-      acc = acc * a + o * wt;
-      Ls = Ls * a + ml[1] * wt;
-      M = Mn;
+      acc += o * wt;
+      Ls += ml[1] * wt;
     }
     for (int off = 1; off < tpp; off <<= 1) {
-      const float Mo = __shfl_xor(M, off);
-      const float Lo = __shfl_xor(Ls, off);
-      f32x4 ao;
+      Ls += __shfl_xor(Ls, off);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) ao[c] = __shfl_xor(acc[c], off);
-      // combine in a fixed order: lower sub first
-      const bool lower = (sub & off) == 0;
-      const float M1 = lower ? M : Mo, M2 = lower ? Mo : M;
-      const float L1 = lower ? Ls : Lo, L2 = lower ? Lo : Ls;
-      const f32x4 A1 = lower ? acc : ao, A2 = lower ? ao : acc;
-      const float Mn = fmaxf(M1, M2);
-      const float Mu = Mn == -INFINITY ? 0.f : Mn;
-      const float e1 = __builtin_amdgcn_exp2f(M1 - Mu), e2 = __builtin_amdgcn_exp2f(M2 - Mu);
-      acc = A1 * e1 + A2 * e2;
-      Ls = L1 * e1 + L2 * e2;
-      M = Mn;
+      for (int c = 0; c < 4; ++c) acc[c] += __shfl_xor(acc[c], off);
     }
     if (sub == 0) {
       const float inv = Ls > 0.f ? 1.0f / Ls : 0.f;
@@ -1179,11 +1171,13 @@ pkv_status paged_attention_decode(const kv_pool* pool, const paged_decode_args* 
   hipLaunchKernelGGL(fn, dim3((uint32_t)grid), dim3(256), lds, s, P);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "decode launch");
-  // few sequences: wide workgroups (many pieces each); many: narrow ones, so
-  // that the dispatch of workgroups with nothing to merge stays cheap
-  const int mthreads = segs <= 512 ? 1024 : 256;
-  hipLaunchKernelGGL(d.head_dim == 64 ? merge_kernel<64> : merge_kernel<128>, dim3((uint32_t)segs),
-                     dim3(mthreads), 0, s, P);
+  // few sequence-heads: spread each one's output positions over several
+  // workgroups so that the merge still uses most CUs
+  const int np = (int)(P.group * (d.head_dim / 4));
+  int pg = 1;
+  while (segs * pg < 512 && np / (pg * 2) >= 16) pg *= 2;
+  hipLaunchKernelGGL(d.head_dim == 64 ? merge_kernel<64> : merge_kernel<128>, dim3((uint32_t)segs, pg),
+                     dim3(256), 0, s, P);
   e = hipGetLastError();
   return e == hipSuccess ? PKV_OK : hip_fail(e, "merge launch");
 }
