@@ -173,6 +173,19 @@ pkv_status block_table_fork_batch(kv_pool* pool, const int32_t* parents, int32_t
  * nothing: an unknown or repeated id changes nothing. */
 pkv_status block_table_free_batch(kv_pool* pool, const int32_t* seqs, int32_t n);
 
+/* Sliding-window release (page "生成一个字…", section "再往后：压 KV 的三条路线":
+ * with a window only the last stretch of tokens is attended, so the cache a
+ * sequence holds can stay bounded by the window): every block of seq whose
+ * tokens all lie before `token` is handed back -- its count drops by one, it
+ * goes to the back of the free queue when that reaches 0 (table order), and
+ * its table entry becomes -1.  Logical positions do not move, so later
+ * tokens keep their slots; decode reads -1 entries as empty blocks.  For a
+ * window W, token = L + 1 - W (L tokens stored now) releases exactly what no
+ * later decode can attend.  0 <= token <= length, else PKV_E_INVAL.
+ * *n_released_out: table entries released by this call. */
+pkv_status block_table_release_before(kv_pool* pool, int32_t seq, int32_t token,
+                                      int32_t* n_released_out);
+
 /* Copy a sequence's table (up to cap entries) and report its block count and
  * token length.  blocks_out may be NULL when cap == 0. */
 pkv_status block_table_get(const kv_pool* pool, int32_t seq, int32_t* blocks_out,

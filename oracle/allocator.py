@@ -30,6 +30,9 @@ Readings where the pages are silent (the C++ library follows the same ones):
 * An append that cannot get every block it needs fails with no change to any
   state (strong guarantee); a batch append is all-or-nothing.
 * Sequence ids count up from 0 and are never reused.
+* Window release (page "生成一个字…", section "再往后：压 KV 的三条路线"): blocks
+  wholly before a given token can be handed back; their table entries become
+  -1 and keep their logical position.
 """
 from collections import deque
 import copy
@@ -173,17 +176,46 @@ class BlockManager:
         self._tables[child] = list(self._tables[parent])
         self._lens[child] = self._lens[parent]
         for blk in self._tables[child]:
-            self._ref[blk] += 1
+            if blk >= 0:
+                self._ref[blk] += 1
         return child
 
     def free(self, seq: int):
         self._check(seq)
         for blk in self._tables[seq]:
+            if blk < 0:
+                continue
             self._ref[blk] -= 1
             if self._ref[blk] == 0:
                 self._free.append(blk)
         del self._tables[seq]
         del self._lens[seq]
+
+    def release_before(self, seq: int, token: int) -> int:
+        """Give back every block of ``seq`` whose tokens all lie before
+        ``token`` (page "生成一个字…", section "再往后：压 KV 的三条路线": with a
+        sliding window only the last stretch of tokens is attended, so the
+        cache a sequence holds is bounded by the window).  A released block's
+        table entry becomes -1; logical positions, and so the slots of later
+        tokens, do not move.  Released blocks go to the back of the free queue
+        in table order once no other sequence holds them.  ``token`` may not
+        exceed the sequence length.  Returns the number of entries released
+        by this call."""
+        self._check(seq)
+        if not 0 <= token <= self._lens[seq]:
+            raise AllocatorError("token must lie in [0, length]")
+        tab = self._tables[seq]
+        n = 0
+        for i in range(token // self.block_size):
+            blk = tab[i]
+            if blk < 0:
+                continue
+            self._ref[blk] -= 1
+            if self._ref[blk] == 0:
+                self._free.append(blk)
+            tab[i] = -1
+            n += 1
+        return n
 
     # ---- dense export ----------------------------------------------------
     def export(self, seqs, max_blocks: int):

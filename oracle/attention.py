@@ -44,15 +44,18 @@ def _key_range(L, window):
     return lo, L
 
 
-def gather_kv(pool, layer, table, L, kv_head):
-    """Contiguous float64 K, V [L][D] of one sequence and KV head."""
+def gather_kv(pool, layer, table, L, kv_head, lo=0):
+    """Contiguous float64 K, V [L - lo][D] of tokens lo .. L-1 of one sequence
+    and KV head.  Only the blocks holding those tokens are read (a sliding
+    window may have released the earlier ones)."""
     bs = pool.block_size
-    nblk = -(-L // bs)
-    blocks = list(table[:nblk])
-    if len(blocks) < nblk or any(b < 0 or b >= pool.num_blocks for b in blocks):
-        raise ValueError("block table does not cover the context length")
-    K = pool.values("k", layer, blocks, kv_head)[:L]
-    V = pool.values("v", layer, blocks, kv_head)[:L]
+    first, nblk = lo // bs, -(-L // bs)
+    blocks = list(table[first:nblk])
+    if len(blocks) < nblk - first or any(b < 0 or b >= pool.num_blocks for b in blocks):
+        raise ValueError("block table does not cover the attended tokens")
+    skip = lo - first * bs
+    K = pool.values("k", layer, blocks, kv_head)[skip:L - first * bs]
+    V = pool.values("v", layer, blocks, kv_head)[skip:L - first * bs]
     return K, V
 
 
@@ -76,8 +79,7 @@ def decode_attention(pool, layer, q, q_dtype, tables, lens, scale, window=0):
         if hi - lo <= 0:
             continue
         for g in range(Hkv):
-            K, V = gather_kv(pool, layer, tables[b], L, g)
-            K, V = K[lo:hi], V[lo:hi]
+            K, V = gather_kv(pool, layer, tables[b], hi, g, lo)
             for h in range(g * G, (g + 1) * G):
                 out[b, h] = _textbook(qf[b, h], K, V, scale)
     return out
@@ -122,8 +124,7 @@ def decode_attention_split(pool, layer, q, q_dtype, tables, lens, scale,
             continue
         cuts = [0] + list(boundaries_fn(hi - lo)) + [hi - lo]
         for g in range(Hkv):
-            K, V = gather_kv(pool, layer, tables[b], L, g)
-            K, V = K[lo:hi], V[lo:hi]
+            K, V = gather_kv(pool, layer, tables[b], hi, g, lo)
             for h in range(g * G, (g + 1) * G):
                 parts = [partial_attention(qf[b, h], K[a:e], V[a:e], scale)
                          for a, e in zip(cuts[:-1], cuts[1:])]

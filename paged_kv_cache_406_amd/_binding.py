@@ -85,6 +85,7 @@ _SIGS = {
     "block_table_free": (c_i32, [P_pool, c_i32]),
     "block_table_fork_batch": (c_i32, [P_pool, P_i32, c_i32, P_i32]),
     "block_table_free_batch": (c_i32, [P_pool, P_i32, c_i32]),
+    "block_table_release_before": (c_i32, [P_pool, c_i32, c_i32, P_i32]),
     "block_table_get": (c_i32, [P_pool, c_i32, P_i32, c_i32, P_i32, P_i32]),
     "block_table_export": (c_i32, [P_pool, P_i32, c_i32, c_i32, P_i32, P_i32]),
     "kv_pool_copy_blocks": (c_i32, [P_pool, c_vp, c_i32, c_vp]),
@@ -240,6 +241,13 @@ def block_table_fork_batch(pool, parents):
 def block_table_free_batch(pool, seqs) -> None:
     arr, arr_p = _i32_array(seqs)
     _check(_lib.block_table_free_batch(pool, arr_p, len(arr)))
+
+
+def block_table_release_before(pool, seq, token) -> int:
+    """Release the blocks of seq wholly before token; returns how many."""
+    out = c_i32()
+    _check(_lib.block_table_release_before(pool, seq, token, ctypes.byref(out)))
+    return out.value
 
 
 def block_table_get(pool, seq):

@@ -331,6 +331,14 @@ __device__ __forceinline__ void write_zero_rows(const DecodeParams& P, int b, in
   }
 }
 
+// 16-byte streaming load: the cache is read once per call, so K/V tiles
+// are loaded non-temporally (no cache allocation for data that is not reused)
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const uint8_t* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // 16 bytes as 8 x 16-bit MFMA operand elements
 template <typename V8>
 __device__ __forceinline__ V8 as8(const uint4& w) {
@@ -483,12 +491,12 @@ struct Decoder {
     for (int t = 0; t < NQT; ++t)
 #pragma unroll
       for (int j = 0; j < NKJ; ++j)
-        T.k[t * NKJ + j] = *reinterpret_cast<const uint4*>(a.krow + (4 * j * BS + 4 * t) * 16);
+        T.k[t * NKJ + j] = load_stream(a.krow + (4 * j * BS + 4 * t) * 16);
   }
 
   static __device__ __forceinline__ void load_v(VTile& T, const Addr& a) {
 #pragma unroll
-    for (int n = 0; n < NV; ++n) T.v[n] = *reinterpret_cast<const uint4*>(a.vrow + 16 * n * BS * EB);
+    for (int n = 0; n < NV; ++n) T.v[n] = load_stream(a.vrow + 16 * n * BS * EB);
     T.tok0 = a.tok0;
     T.ok = a.ok;
   }

@@ -265,7 +265,8 @@ pkv_status block_table_fork(kv_pool* p, int32_t parent, int32_t* child_out) {
   Sequence child = it->second;  // copy first: may throw, state untouched
   const int32_t id = p->next_id;
   auto res = p->seqs.emplace(id, std::move(child));
-  for (int32_t b : res.first->second.table) p->refcount[b] += 1;
+  for (int32_t b : res.first->second.table)
+    if (b >= 0) p->refcount[b] += 1;
   p->next_id++;
   *child_out = id;
   return PKV_OK;
@@ -278,12 +279,33 @@ pkv_status block_table_free(kv_pool* p, int32_t seq) {
   auto it = p->seqs.find(seq);
   if (it == p->seqs.end()) return fail(PKV_E_INVAL, "unknown sequence id");
   for (int32_t b : it->second.table) {
+    if (b < 0) continue;
     p->refcount[b] -= 1;
     if (p->refcount[b] == 0) push_free(p, b);
   }
   p->seqs.erase(it);
   return PKV_OK;
   PKV_GUARD_END
+}
+
+pkv_status block_table_release_before(kv_pool* p, int32_t seq, int32_t token, int32_t* n_released_out) {
+  if (!p || !n_released_out) return fail(PKV_E_INVAL, "null argument");
+  auto it = p->seqs.find(seq);
+  if (it == p->seqs.end()) return fail(PKV_E_INVAL, "unknown sequence id");
+  Sequence& s = it->second;
+  if (token < 0 || token > s.len) return fail(PKV_E_INVAL, "token must lie in [0, length]");
+  int32_t n = 0;
+  const int64_t nblk = token / p->desc.block_size;
+  for (int64_t i = 0; i < nblk; ++i) {
+    const int32_t b = s.table[i];
+    if (b < 0) continue;
+    p->refcount[b] -= 1;
+    if (p->refcount[b] == 0) push_free(p, b);
+    s.table[i] = -1;
+    ++n;
+  }
+  *n_released_out = n;
+  return PKV_OK;
 }
 
 pkv_status block_table_fork_batch(kv_pool* p, const int32_t* parents, int32_t n, int32_t* children_out) {
@@ -308,7 +330,8 @@ pkv_status block_table_fork_batch(kv_pool* p, const int32_t* parents, int32_t n,
     throw;
   }
   for (int32_t i = 0; i < n; ++i) {
-    for (int32_t b : p->seqs.find(id0 + i)->second.table) p->refcount[b] += 1;
+    for (int32_t b : p->seqs.find(id0 + i)->second.table)
+      if (b >= 0) p->refcount[b] += 1;
     children_out[i] = id0 + i;
   }
   p->next_id += n;
@@ -330,6 +353,7 @@ pkv_status block_table_free_batch(kv_pool* p, const int32_t* seqs, int32_t n) {
   }
   for (auto it : its) {
     for (int32_t b : it->second.table) {
+      if (b < 0) continue;
       p->refcount[b] -= 1;
       if (p->refcount[b] == 0) push_free(p, b);
     }

@@ -85,11 +85,15 @@ def test_block_manager_matches_oracle(seed):
                 okids = [bm.fork(ids[p]) for p in parents]
                 assert kids == okids
                 ids.update(zip(kids, okids))
-            elif op < 0.32:
+            elif op < 0.29:
                 s = rng.choice(live)
                 P.block_table_free(h, s)
                 bm.free(ids[s])
                 del ids[s]
+            elif op < 0.32:
+                s = rng.choice(live)
+                tok = rng.randint(0, bm.length(ids[s]))
+                assert P.block_table_release_before(h, s, tok) == bm.release_before(ids[s], tok)
             elif op < 0.35:
                 # batch free: the same as freeing each sequence in order
                 batch = rng.sample(live, rng.randint(1, len(live)))

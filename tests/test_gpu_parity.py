@@ -286,3 +286,33 @@ def test_workspace_reused_across_calls():
             if B == w.batch:
                 assert np.array_equal(got, fresh[s]), (rep, s, B)
             assert np.abs(got - ref[:B]).max() <= TOL[w.kv_dtype], (rep, s, B)
+
+
+@pytest.mark.parametrize("window", [16, 40, 100])
+def test_window_release_decodes_the_same(window):
+    # releasing every block wholly before the window (block_table_release_before)
+    # leaves -1 table entries that decode never reads: outputs are bitwise
+    # unchanged, tables and free queue match the oracle's
+    w = CASES["gqa8_bf16"]
+    d = wl.draw(w)
+    ost = OracleState(w, d)
+    gst = GpuState(w, d)
+    try:
+        q = wl.q_bits(w)
+        tables, lens = gst.export()
+        before = {s: gst.decode(q, tables, lens, num_splits=s, window=window) for s in (1, 0, 3)}
+        h = gst.pool.handle
+        for s, os_, L in zip(gst.seqs, ost.seqs, lens):
+            tok = max(0, int(L) - window)
+            assert P.block_table_release_before(h, s, tok) == ost.bm.release_before(os_, tok)
+        assert P.kv_pool_free_list(h) == ost.bm.free_list()
+        t2, l2 = gst.export()
+        ot2, ol2 = ost.export()
+        assert np.array_equal(t2, ot2) and (t2 == -1).sum() > 0
+        ref = _oracle_out(ost, q, ot2, ol2, window=window)
+        for s in (1, 0, 3):
+            got = gst.decode(q, t2, l2, num_splits=s, window=window)
+            assert np.array_equal(got, before[s]), s
+            assert np.abs(got - ref).max() <= TOL[w.kv_dtype]
+    finally:
+        gst.close()

@@ -169,8 +169,8 @@ def _check_invariants(bm):
     nb = bm.num_blocks
     refs = [bm.refcount(b) for b in range(nb)]
     seqs = bm.sequences()
-    # sum of reference counts = total table entries
-    assert sum(refs) == sum(len(bm.table(s)) for s in seqs)
+    # sum of reference counts = total (non-released) table entries
+    assert sum(refs) == sum(sum(1 for b in bm.table(s) if b >= 0) for s in seqs)
     # free and referenced blocks partition the pool
     free = bm.free_list()
     assert len(set(free)) == len(free)
@@ -186,6 +186,7 @@ def _random_ops(seed, nb, bs, steps):
     bm = BlockManager(nb, bs, free_order=order)
     memory = {}              # slot -> token id
     logical = {}             # seq -> list of token ids (the block-free model)
+    gone = {}                # seq -> tokens before this index were released
     next_tok = 0
     for _ in range(steps):
         live = bm.sequences()
@@ -193,14 +194,26 @@ def _random_ops(seed, nb, bs, steps):
         if op < 0.1 or not live:
             s = bm.alloc()
             logical[s] = []
-        elif op < 0.25:
+            gone[s] = 0
+        elif op < 0.22:
             p = rng.choice(live)
             c = bm.fork(p)
             logical[c] = list(logical[p])
-        elif op < 0.35:
+            gone[c] = gone[p]
+        elif op < 0.3:
             s = rng.choice(live)
             bm.free(s)
             del logical[s]
+        elif op < 0.35:
+            # window release: whole blocks before a token go back to the pool
+            s = rng.choice(live)
+            tok = rng.randint(0, bm.length(s))
+            before = sum(1 for b in bm.table(s) if b >= 0)
+            n = bm.release_before(s, tok)
+            new_gone = max(gone[s], (tok // bs) * bs)
+            assert n == before - sum(1 for b in bm.table(s) if b >= 0)
+            assert n == (new_gone - gone[s]) // bs
+            gone[s] = new_gone
         elif op < 0.5:
             batch = rng.sample(live, rng.randint(1, len(live)))
             try:
@@ -241,8 +254,9 @@ def _random_ops(seed, nb, bs, steps):
         # read every sequence back through its table
         for s in bm.sequences():
             tab = bm.table(s)
-            got = [memory[tab[t // bs] * bs + t % bs] for t in range(bm.length(s))]
-            assert got == logical[s], (seed, s)
+            assert all(b < 0 for b in tab[:gone[s] // bs]) and all(b >= 0 for b in tab[gone[s] // bs:])
+            got = [memory[tab[t // bs] * bs + t % bs] for t in range(gone[s], bm.length(s))]
+            assert got == logical[s][gone[s]:], (seed, s)
 
 
 @pytest.mark.parametrize("seed", range(40))
@@ -265,3 +279,25 @@ def test_export_pads_with_minus_one():
     assert lens.tolist() == [1, 5]
     with pytest.raises(AllocatorError):
         bm.export([a], 1)
+
+
+def test_window_release_bounds_held_blocks():
+    # page "生成一个字…", section "再往后：压 KV 的三条路线": with a sliding window
+    # the cache a sequence holds is bounded by the window, not the context.
+    # Decoding 1000 tokens with a 64-token window and releasing after every
+    # step never holds more than ceil(64/16) + 1 blocks.
+    bs, W = 16, 64
+    bm = BlockManager(8, bs)
+    s = bm.alloc()
+    for n in range(1, 1001):
+        bm.append(s, 1)
+        bm.release_before(s, max(0, n + 1 - W))
+        held = sum(1 for b in bm.table(s) if b >= 0)
+        assert held <= -(-W // bs) + 1
+        assert len(bm.table(s)) == -(-n // bs)
+    # released entries keep their logical position: the next token's slot is
+    # still table[n // bs] * bs + n % bs
+    slots, _ = bm.append(s, 1)
+    assert slots[0] == bm.table(s)[1000 // bs] * bs + 1000 % bs
+    with pytest.raises(AllocatorError):
+        bm.release_before(s, 1002)

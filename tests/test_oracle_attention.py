@@ -264,3 +264,26 @@ def test_fp8_decode_uses_codes_times_scale():
     stb = OracleState(wb, d)
     ob = decode_attention(stb.pool, 0, q, "bf16", tables, lens, 0.25)
     assert np.abs(out - ob).max() < 0.15
+
+
+@pytest.mark.parametrize("window", [1, 16, 17, 24])
+def test_window_reads_only_the_window(window):
+    # page "生成一个字…", section "再往后：压 KV 的三条路线": the query attends the
+    # last stretch only, so releasing every block wholly before it (table
+    # entries -1) leaves the result bitwise unchanged
+    w = wl.WORKLOADS["c1"]
+    d = wl.draw(w)
+    st = OracleState(w, d)
+    q = wl.q_bits(w)
+    tables, lens = st.export()
+    scale = 1.0 / math.sqrt(w.head_dim)
+    before = decode_attention(st.pool, 0, q, w.q_dtype, tables, lens, scale, window)
+    for s, L in zip(st.seqs, lens):
+        st.bm.release_before(s, max(0, int(L) - window))
+    t2, l2 = st.export()
+    assert (t2 == -1).sum() > (tables == -1).sum()
+    after = decode_attention(st.pool, 0, q, w.q_dtype, t2, l2, scale, window)
+    assert np.array_equal(before, after)
+    # without the window the released blocks are needed: the gather refuses
+    with pytest.raises(ValueError):
+        decode_attention(st.pool, 0, q, w.q_dtype, t2, l2, scale, 0)

@@ -136,3 +136,41 @@ def test_e4m3_wrong_bias_is_caught(monkeypatch):
     monkeypatch.setattr(e4m3_mod, "_EXP_BIAS", 8)
     monkeypatch.setattr(TE, "e4m3_decode_table", e4m3_mod.e4m3_decode_table)
     assert _fails(TE.test_special_values_from_format_definition)
+
+
+def test_release_one_block_too_many_is_caught(monkeypatch):
+    # release the block that contains `token` as well (off by one)
+    def too_many(self, seq, token):
+        self._check(seq)
+        tab = self._tables[seq]
+        n = 0
+        for i in range(min(len(tab), token // self.block_size + 1)):
+            blk = tab[i]
+            if blk < 0:
+                continue
+            self._ref[blk] -= 1
+            if self._ref[blk] == 0:
+                self._free.append(blk)
+            tab[i] = -1
+            n += 1
+        return n
+    monkeypatch.setattr(alloc_mod.BlockManager, "release_before", too_many)
+    pins = [lambda s=s: TA.test_random_ops_tiny_pools(s) for s in range(20)] + \
+           [TA.test_window_release_bounds_held_blocks]
+    assert _any_fails(pins)
+
+
+def test_release_without_freeing_is_caught(monkeypatch):
+    # mark entries released but never give the blocks back
+    def leak(self, seq, token):
+        tab = self._tables[seq]
+        n = 0
+        for i in range(token // self.block_size):
+            if tab[i] >= 0:
+                tab[i] = -1
+                n += 1
+        return n
+    monkeypatch.setattr(alloc_mod.BlockManager, "release_before", leak)
+    pins = [lambda s=s: TA.test_random_ops_tiny_pools(s) for s in range(20)] + \
+           [TA.test_window_release_bounds_held_blocks]
+    assert _any_fails(pins)
