@@ -20,6 +20,7 @@ timed on a bounded sample of the same workload.
     python bench.py [--steps K] [--warmup W] [--workload c3]
 """
 import argparse
+import gc
 import json
 import math
 import os
@@ -220,20 +221,35 @@ def run(args):
                                sliding_window=w.window, num_splits=args.splits)
     ws_bytes = P.paged_attention_workspace_size(reps[0].pool.handle, args0)
     ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
-    # pinned staging ring for the per-step metadata
+    # pinned staging ring for the per-step metadata; each buffer is reused once
+    # the upload that last read it has run
     ring = []
     for _ in range(4):
         buf = torch.empty(reps[0].n_meta, dtype=torch.int32, pin_memory=True)
-        ring.append((buf, buf.numpy(), torch.cuda.Event()))
+        ring.append((buf, buf.numpy()))
     mb = reps[0].max_blocks
-    dev_ev = []
+    meta_bytes = reps[0].n_meta * 4
     prefix = w.lengths_kind == "prefix"
+    n_total = args.warmup + args.steps
+    # per-step decode arguments and timing events, made before the timed loop
+    dec_args = []
+    for t in range(n_total):
+        rep = reps[t % len(reps)]
+        dec_args.append(P.make_decode_args(0, B, w.num_q_heads, mb, steps[t][2], w.q_dtype, rep.d_tables,
+                                           rep.d_lens, scale, out, "f32", sliding_window=w.window,
+                                           num_splits=args.splits, workspace=ws, workspace_bytes=ws_bytes))
+    # events around each decode; the one after step t's decode also tells the
+    # host that step t's upload has run, so its staging buffer may be rewritten
+    ev_pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(n_total)]
+    dev_lens = []
 
     def step(t, record):
         rep = reps[t % len(reps)]
         h = rep.pool.handle
-        buf, npb, ev = ring[t % len(ring)]
-        ev.synchronize()                       # the copy that last used this buffer is done
+        buf, npb = ring[t % len(ring)]
+        if t >= len(ring):
+            ev_pairs[t - len(ring)][1].synchronize()
         slots_np = npb[: 2 * B].view(np.int64)
         cows_np = npb[2 * B: 4 * B].reshape(B, 2)
         tables_np = npb[4 * B: 4 * B + B * mb].reshape(B, mb)
@@ -242,30 +258,22 @@ def run(args):
             # a sampling branch per sequence: fork, append (copy-on-write of the
             # shared partial last block), decode, free
             seqs = P.block_table_fork_batch(h, rep.seq_arr)
-            lens_now = rep.lengths + 1
         else:
             seqs = rep.seq_arr
             rep.lengths += 1
-            lens_now = rep.lengths
         _, cows = P.block_table_append_batch(h, seqs, slots_out=slots_np, cow_out=cows_np)
         P.block_table_export(h, seqs, mb, tables_out=tables_np, lens_out=lens_np)
-        rep.meta.copy_(buf, non_blocking=True)
-        ev.record(stream)
+        P.kv_metadata_upload(rep.meta, buf, meta_bytes, sptr)
         if len(cows):
             P.kv_pool_copy_blocks(h, rep.d_cows, len(cows), sptr)
-        kd, vd, qd = steps[t]
+        kd, vd, _ = steps[t]
         P.paged_kv_append(h, 0, kd, vd, w.src_dtype, rep.d_slots, B, sptr)
-        a = P.make_decode_args(0, B, w.num_q_heads, mb, qd, w.q_dtype, rep.d_tables, rep.d_lens,
-                               scale, out, "f32", sliding_window=w.window, num_splits=args.splits,
-                               workspace=ws, workspace_bytes=ws_bytes)
+        e0, e1 = ev_pairs[t]
+        e0.record(stream)
+        P.paged_attention_decode(h, dec_args[t], sptr)
+        e1.record(stream)
         if record:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            P.paged_attention_decode(h, a, sptr)
-            e1.record(stream)
-            dev_ev.append((e0, e1, lens_now.copy()))
-        else:
-            P.paged_attention_decode(h, a, sptr)
+            dev_lens.append(rep.lengths + 1 if prefix else rep.lengths.copy())
         if prefix:
             # host bookkeeping only: stream order keeps this step's kernels ahead
             # of any later reuse of the freed blocks
@@ -275,6 +283,11 @@ def run(args):
     for t in range(args.warmup):
         step(t, False)
     torch.cuda.synchronize()
+    # no garbage-collector pass inside the timed loop: a full pass over this
+    # process's objects takes tens of milliseconds
+    gc.collect()
+    gc.freeze()
+    gc.disable()
     log(f"timing {args.steps} steps")
     t_start = torch.cuda.Event(enable_timing=True)
     t_stop = torch.cuda.Event(enable_timing=True)
@@ -285,6 +298,9 @@ def run(args):
     t_stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    gc.enable()
+    gc.unfreeze()
+    dev_ev = [(e0, e1, lens) for (e0, e1), lens in zip(ev_pairs[args.warmup:], dev_lens)]
     step_ms = t_start.elapsed_time(t_stop) / args.steps
     dec_ms = [e0.elapsed_time(e1) for e0, e1, _ in dev_ev]
     dec_bytes = [decode_bytes(w, lens)[0] for _, _, lens in dev_ev]

@@ -207,6 +207,20 @@ pkv_status block_table_export(const kv_pool* pool, const int32_t* seqs, int32_t 
 pkv_status kv_pool_copy_blocks(kv_pool* pool, const kv_block_copy* d_pairs, int32_t n,
                                pkv_stream stream);
 
+/* Per-step metadata to the device (page "AI 陪读顶会论文（三）", section
+ * "PagedAttention 的破局哲学": the kernel finds each sequence's blocks through
+ * its block table, so the tables, lengths and new slots built on the host
+ * must reach device memory before the step's kernels run).  Copies `bytes`
+ * from h_src to d_dst in stream order, by a kernel on `stream` (no copy
+ * engine, so no hand-off between hardware queues around the copy).
+ * h_src: page-locked host memory (hipHostMalloc, or a torch tensor made with
+ * pin_memory=True); [h_src, h_src + bytes) must lie inside one such
+ * allocation.  d_dst: device memory, [d_dst, d_dst + bytes) inside one
+ * allocation.  Both 8-byte aligned, bytes a multiple of 4, else PKV_E_INVAL.
+ * The host must leave h_src unchanged until the copy has run (record an event
+ * after this call and wait on it before rewriting the buffer). */
+pkv_status kv_metadata_upload(void* d_dst, const void* h_src, size_t bytes, pkv_stream stream);
+
 /* Write the new tokens' K and V into their slots of one layer (page
  * "AI 陪读顶会论文（三）", section "为什么自回归解码…必须使用 KV Cache").
  * d_k, d_v: device [n_tokens][num_kv_heads][head_dim] of src_dtype.

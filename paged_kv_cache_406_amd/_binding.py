@@ -80,15 +80,16 @@ _SIGS = {
     "kv_pool_free_list": (c_i32, [P_pool, P_i32, c_i32, P_i32]),
     "block_table_alloc": (c_i32, [P_pool, P_i32]),
     "block_table_append": (c_i32, [P_pool, c_i32, c_i32, P_i64, P_copy, P_i32]),
-    "block_table_append_batch": (c_i32, [P_pool, P_i32, c_i32, P_i64, P_copy, P_i32]),
+    "block_table_append_batch": (c_i32, [P_pool, c_vp, c_i32, c_vp, c_vp, P_i32]),
     "block_table_fork": (c_i32, [P_pool, c_i32, P_i32]),
     "block_table_free": (c_i32, [P_pool, c_i32]),
-    "block_table_fork_batch": (c_i32, [P_pool, P_i32, c_i32, P_i32]),
-    "block_table_free_batch": (c_i32, [P_pool, P_i32, c_i32]),
+    "block_table_fork_batch": (c_i32, [P_pool, c_vp, c_i32, c_vp]),
+    "block_table_free_batch": (c_i32, [P_pool, c_vp, c_i32]),
     "block_table_release_before": (c_i32, [P_pool, c_i32, c_i32, P_i32]),
     "block_table_get": (c_i32, [P_pool, c_i32, P_i32, c_i32, P_i32, P_i32]),
-    "block_table_export": (c_i32, [P_pool, P_i32, c_i32, c_i32, P_i32, P_i32]),
+    "block_table_export": (c_i32, [P_pool, c_vp, c_i32, c_i32, c_vp, c_vp]),
     "kv_pool_copy_blocks": (c_i32, [P_pool, c_vp, c_i32, c_vp]),
+    "kv_metadata_upload": (c_i32, [c_vp, c_vp, c_size, c_vp]),
     "paged_kv_append": (c_i32, [P_pool, c_i32, c_vp, c_vp, c_i32, c_vp, c_i32, c_vp]),
     "paged_attention_workspace_size": (c_i32, [P_pool, ctypes.POINTER(paged_decode_args), ctypes.POINTER(c_size)]),
     "paged_attention_decode": (c_i32, [P_pool, ctypes.POINTER(paged_decode_args), c_vp]),
@@ -132,6 +133,19 @@ def _stream(stream):
 def _i32_array(values):
     arr = np.ascontiguousarray(values, dtype=np.int32)
     return arr, arr.ctypes.data_as(P_i32)
+
+
+def _i32_addr(values):
+    """(array, address) of values as contiguous int32; no copy if they already are."""
+    arr = np.ascontiguousarray(values, dtype=np.int32)
+    return arr, arr.ctypes.data
+
+
+def _out_addr(arr, dtype, shape_n, what):
+    """Address of a caller-provided output buffer after checking it fits."""
+    if arr.dtype != dtype or not arr.flags.c_contiguous or arr.size < shape_n:
+        raise ValueError(f"{what} must be a C-contiguous {np.dtype(dtype).name} array of >= {shape_n} elements")
+    return arr.ctypes.data
 
 
 # ---- pool ---------------------------------------------------------------
@@ -210,13 +224,13 @@ def block_table_append_batch(pool, seqs, slots_out=None, cow_out=None):
     """One token for each sequence.  Returns (slots int64 [n], cow pairs int32 [k][2]).
     Optional preallocated ``slots_out`` (int64 [n]) and ``cow_out`` (int32 [n][2])
     numpy buffers are filled in place."""
-    seq_arr, seq_p = _i32_array(seqs)
+    seq_arr, seq_p = _i32_addr(seqs)
     n = len(seq_arr)
     slots = slots_out if slots_out is not None else np.zeros(max(n, 1), dtype=np.int64)
     cows = cow_out if cow_out is not None else np.zeros((max(n, 1), 2), dtype=np.int32)
     ncow = c_i32()
-    _check(_lib.block_table_append_batch(pool, seq_p, n, slots.ctypes.data_as(P_i64),
-                                         cows.ctypes.data_as(P_copy), ctypes.byref(ncow)))
+    _check(_lib.block_table_append_batch(pool, seq_p, n, _out_addr(slots, np.int64, n, "slots_out"),
+                                         _out_addr(cows, np.int32, 2 * n, "cow_out"), ctypes.byref(ncow)))
     return slots[:n], cows[:ncow.value]
 
 
@@ -232,14 +246,14 @@ def block_table_free(pool, seq) -> None:
 
 def block_table_fork_batch(pool, parents):
     """Children (int32 [n]) of the given parents, in order."""
-    par, par_p = _i32_array(parents)
+    par, par_p = _i32_addr(parents)
     out = np.zeros(max(len(par), 1), dtype=np.int32)
-    _check(_lib.block_table_fork_batch(pool, par_p, len(par), out.ctypes.data_as(P_i32)))
+    _check(_lib.block_table_fork_batch(pool, par_p, len(par), out.ctypes.data))
     return out[:len(par)]
 
 
 def block_table_free_batch(pool, seqs) -> None:
-    arr, arr_p = _i32_array(seqs)
+    arr, arr_p = _i32_addr(seqs)
     _check(_lib.block_table_free_batch(pool, arr_p, len(arr)))
 
 
@@ -263,18 +277,24 @@ def block_table_get(pool, seq):
 def block_table_export(pool, seqs, max_blocks, tables_out=None, lens_out=None):
     """Returns (tables int32 [n][max_blocks] padded with -1, lens int32 [n]).
     Optional numpy output buffers (e.g. views of pinned memory) are filled."""
-    seq_arr, seq_p = _i32_array(seqs)
+    seq_arr, seq_p = _i32_addr(seqs)
     n = len(seq_arr)
     tables = tables_out if tables_out is not None else np.zeros((n, max_blocks), dtype=np.int32)
     lens = lens_out if lens_out is not None else np.zeros(n, dtype=np.int32)
-    _check(_lib.block_table_export(pool, seq_p, n, max_blocks, tables.ctypes.data_as(P_i32),
-                                   lens.ctypes.data_as(P_i32)))
+    _check(_lib.block_table_export(pool, seq_p, n, max_blocks, _out_addr(tables, np.int32, n * max_blocks, "tables_out"),
+                                   _out_addr(lens, np.int32, n, "lens_out")))
     return tables, lens
 
 
 # ---- device work ------------------------------------------------------------
 def kv_pool_copy_blocks(pool, d_pairs, n, stream=None) -> None:
     _check(_lib.kv_pool_copy_blocks(pool, _ptr(d_pairs), n, _stream(stream)))
+
+
+def kv_metadata_upload(d_dst, h_src, nbytes, stream=None) -> None:
+    """Copy nbytes from page-locked host memory (a pinned tensor or address) to
+    device memory with a kernel on the stream."""
+    _check(_lib.kv_metadata_upload(_ptr(d_dst), _ptr(h_src), nbytes, _stream(stream)))
 
 
 def paged_kv_append(pool, layer, d_k, d_v, src_dtype, d_slots, n_tokens, stream=None) -> None:

@@ -47,6 +47,7 @@
 //    that each XCD (one L2) gets a contiguous run of ranges.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <mutex>
@@ -910,6 +911,33 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams P) {
 }
 
 // ---------------------------------------------------------------------------
+// metadata upload: page-locked host memory -> device memory, by a kernel
+// ---------------------------------------------------------------------------
+// A copy engine would need a hand-off between two hardware queues before and
+// after the copy; a kernel on the caller's stream is ordered like the kernels
+// around it.  The loads are system-scope atomics, so they see what the host
+// wrote before the launch whatever the GPU caches hold.
+__global__ __launch_bounds__(256) void upload_kernel(const uint64_t* __restrict__ src,
+                                                     uint64_t* __restrict__ dst, int64_t n8,
+                                                     const uint32_t* __restrict__ src_tail,
+                                                     uint32_t* __restrict__ dst_tail) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n8; i += 4 * stride) {
+    uint64_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      v[u] = __hip_atomic_load(src + i + u * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) dst[i + u * stride] = v[u];
+  }
+  for (; i < n8; i += stride)
+    dst[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  if (src_tail && blockIdx.x == 0 && threadIdx.x == 0)
+    *dst_tail = __hip_atomic_load(src_tail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 static constexpr int kWavesPerCU = 4;
@@ -1040,6 +1068,48 @@ pkv_status kv_pool_copy_blocks(kv_pool* pool, const kv_block_copy* d_pairs, int3
                      (uint8_t*)d.k_cache, (uint8_t*)d.v_cache, d_pairs, (int64_t)d.num_blocks, tile_bytes);
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? PKV_OK : hip_fail(e, "copy_blocks launch");
+}
+
+// [p, p + bytes) lies inside one HIP allocation of the wanted kind.
+static bool in_one_allocation(const void* p, size_t bytes, hipMemoryType kind) {
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  if (at.type != kind) return false;
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)p) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  const uintptr_t b = reinterpret_cast<uintptr_t>(base), q = reinterpret_cast<uintptr_t>(p);
+  return q >= b && bytes <= size && q - b <= size - bytes;
+}
+
+pkv_status kv_metadata_upload(void* d_dst, const void* h_src, size_t bytes, pkv_stream stream) {
+  if (bytes == 0) return PKV_OK;
+  if (!d_dst || !h_src) return fail(PKV_E_INVAL, "null pointer");
+  if (reinterpret_cast<uintptr_t>(d_dst) % 8 || reinterpret_cast<uintptr_t>(h_src) % 8 || bytes % 4)
+    return fail(PKV_E_INVAL, "src and dst must be 8-byte aligned and bytes a multiple of 4");
+  if (!in_one_allocation(h_src, bytes, hipMemoryTypeHost))
+    return fail(PKV_E_INVAL, "src is not inside one page-locked host allocation");
+  if (!in_one_allocation(d_dst, bytes, hipMemoryTypeDevice))
+    return fail(PKV_E_INVAL, "dst is not inside one device allocation");
+  hipPointerAttribute_t at;
+  hipError_t e = hipPointerGetAttributes(&at, h_src);
+  if (e != hipSuccess || !at.devicePointer) return hip_fail(e, "hipPointerGetAttributes");
+  const uint64_t* src = static_cast<const uint64_t*>(at.devicePointer);
+  uint64_t* dst = static_cast<uint64_t*>(d_dst);
+  const int64_t n8 = (int64_t)(bytes / 8);
+  const uint32_t* src_tail = bytes % 8 ? reinterpret_cast<const uint32_t*>(src + n8) : nullptr;
+  uint32_t* dst_tail = bytes % 8 ? reinterpret_cast<uint32_t*>(dst + n8) : nullptr;
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((n8 + 1023) / 1024, 1024));
+  hipLaunchKernelGGL(upload_kernel, dim3((uint32_t)blocks), dim3(256), 0, (hipStream_t)stream, src, dst, n8,
+                     src_tail, dst_tail);
+  e = hipGetLastError();
+  return e == hipSuccess ? PKV_OK : hip_fail(e, "upload launch");
 }
 
 pkv_status paged_kv_append(kv_pool* pool, int32_t layer, const void* d_k, const void* d_v,

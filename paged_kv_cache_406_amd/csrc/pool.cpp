@@ -63,6 +63,28 @@ static inline int64_t blocks_needed(const Sequence& s, int64_t n, int32_t bs,
   return (after - before) + (*cow ? 1 : 0);
 }
 
+// Room for `more` table entries, growing geometrically so that a sequence
+// that gains one block at a time reallocates O(log n) times.
+static inline void reserve_more(std::vector<int32_t>& t, int64_t more) {
+  const size_t want = t.size() + (size_t)more;
+  if (t.capacity() < want) t.reserve(std::max<size_t>({want, 2 * t.capacity(), 16}));
+}
+
+// Resolves a batch of sequence ids into p->batch, rejecting unknown and
+// repeated ids.
+static pkv_status resolve_batch(kv_pool* p, const int32_t* seqs, int32_t n) {
+  const uint64_t stamp = ++p->stamp;
+  p->batch.resize(n);
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = p->seqs.find(seqs[i]);
+    if (it == p->seqs.end()) return fail(PKV_E_INVAL, "unknown sequence id in batch");
+    if (it->second.mark == stamp) return fail(PKV_E_INVAL, "duplicate sequence in batch");
+    it->second.mark = stamp;
+    p->batch[i] = &it->second;
+  }
+  return PKV_OK;
+}
+
 // Performs an append whose block needs were checked; cannot fail.
 static void do_append(kv_pool* p, Sequence& s, int64_t n, int64_t* slots,
                       kv_block_copy* cow, int32_t* n_cow) {
@@ -210,7 +232,7 @@ pkv_status block_table_append(kv_pool* p, int32_t seq, int32_t n_tokens, int64_t
   const int64_t need = blocks_needed(s, n_tokens, bs, last_ref, &cow);
   // the table grows by at most `need` entries: reserve first so that the
   // mutation below cannot throw
-  s.table.reserve(s.table.size() + need);
+  reserve_more(s.table, need);
   if (need > p->count) return fail(PKV_E_OOM, "not enough free blocks");
   *n_cow_out = 0;
   do_append(p, s, n_tokens, slots_out, cow_out, n_cow_out);
@@ -225,33 +247,38 @@ pkv_status block_table_append_batch(kv_pool* p, const int32_t* seqs, int32_t n,
   if (!p || !n_cow_out || n < 0 || (n > 0 && (!seqs || !slots_out || !cow_out)))
     return fail(PKV_E_INVAL, "bad argument");
   const int32_t bs = p->desc.block_size;
-  // dry run: resolve ids, reject duplicates, count blocks with the reference
-  // counts the earlier sequences of the batch leave behind
-  std::vector<Sequence*> ptrs(n);
-  std::unordered_map<int32_t, int32_t> ref_delta;
-  std::unordered_map<int32_t, char> seen;
+  pkv_status st = resolve_batch(p, seqs, n);
+  if (st != PKV_OK) return st;
+  if (p->ref_delta.size() != (size_t)p->desc.num_blocks) p->ref_delta.assign(p->desc.num_blocks, 0);
+  // dry run: count blocks with the reference counts the earlier sequences of
+  // the batch leave behind (a shared last block copied by one of them has one
+  // holder fewer for the next)
   int64_t need = 0;
   for (int32_t i = 0; i < n; ++i) {
-    auto it = p->seqs.find(seqs[i]);
-    if (it == p->seqs.end()) return fail(PKV_E_INVAL, "unknown sequence id in batch");
-    if (!seen.emplace(seqs[i], 1).second) return fail(PKV_E_INVAL, "duplicate sequence in batch");
-    Sequence& s = it->second;
-    if (s.len + 1 > (int64_t)INT32_MAX) return fail(PKV_E_INVAL, "sequence too long");
-    ptrs[i] = &s;
+    Sequence& s = *p->batch[i];
+    if (s.len + 1 > (int64_t)INT32_MAX) {
+      need = -1;
+      break;
+    }
     int32_t last_ref = 0;
     if (s.len % bs) {
       const int32_t last = s.table.back();
-      auto d = ref_delta.find(last);
-      last_ref = p->refcount[last] + (d == ref_delta.end() ? 0 : d->second);
+      last_ref = p->refcount[last] + p->ref_delta[last];
     }
     bool cow = false;
     need += blocks_needed(s, 1, bs, last_ref, &cow);
-    if (cow) ref_delta[s.table.back()] -= 1;
+    if (cow) {
+      if (p->ref_delta[s.table.back()] == 0) p->touched.push_back(s.table.back());
+      p->ref_delta[s.table.back()] -= 1;
+    }
   }
+  for (int32_t b : p->touched) p->ref_delta[b] = 0;
+  p->touched.clear();
+  if (need < 0) return fail(PKV_E_INVAL, "sequence too long");
   if (need > p->count) return fail(PKV_E_OOM, "not enough free blocks");
-  for (int32_t i = 0; i < n; ++i) ptrs[i]->table.reserve(ptrs[i]->table.size() + 1);
+  for (int32_t i = 0; i < n; ++i) reserve_more(p->batch[i]->table, 1);
   *n_cow_out = 0;
-  for (int32_t i = 0; i < n; ++i) do_append(p, *ptrs[i], 1, slots_out + i, cow_out, n_cow_out);
+  for (int32_t i = 0; i < n; ++i) do_append(p, *p->batch[i], 1, slots_out + i, cow_out, n_cow_out);
   return PKV_OK;
   PKV_GUARD_END
 }
@@ -342,23 +369,16 @@ pkv_status block_table_fork_batch(kv_pool* p, const int32_t* parents, int32_t n,
 pkv_status block_table_free_batch(kv_pool* p, const int32_t* seqs, int32_t n) {
   PKV_GUARD_BEGIN
   if (!p || n < 0 || (n > 0 && !seqs)) return fail(PKV_E_INVAL, "bad argument");
-  std::vector<std::unordered_map<int32_t, Sequence>::iterator> its;
-  its.reserve(n);
-  std::unordered_map<int32_t, char> seen;
+  pkv_status st = resolve_batch(p, seqs, n);
+  if (st != PKV_OK) return st;
   for (int32_t i = 0; i < n; ++i) {
-    auto it = p->seqs.find(seqs[i]);
-    if (it == p->seqs.end()) return fail(PKV_E_INVAL, "unknown sequence id in batch");
-    if (!seen.emplace(seqs[i], 1).second) return fail(PKV_E_INVAL, "duplicate sequence in batch");
-    its.push_back(it);
-  }
-  for (auto it : its) {
-    for (int32_t b : it->second.table) {
+    for (int32_t b : p->batch[i]->table) {
       if (b < 0) continue;
       p->refcount[b] -= 1;
       if (p->refcount[b] == 0) push_free(p, b);
     }
-    p->seqs.erase(it);
   }
+  for (int32_t i = 0; i < n; ++i) p->seqs.erase(seqs[i]);
   return PKV_OK;
   PKV_GUARD_END
 }
@@ -382,22 +402,24 @@ pkv_status block_table_export(const kv_pool* p, const int32_t* seqs, int32_t n,
   if (!p || n < 0 || max_blocks < 0 ||
       (n > 0 && (!seqs || !lens_out || (max_blocks > 0 && !tables_out))))
     return fail(PKV_E_INVAL, "bad argument");
-  std::vector<const Sequence*> ptrs(n);
+  PKV_GUARD_BEGIN
+  p->batch.resize(n);
   for (int32_t i = 0; i < n; ++i) {
-    auto it = p->seqs.find(seqs[i]);
+    auto it = const_cast<kv_pool*>(p)->seqs.find(seqs[i]);
     if (it == p->seqs.end()) return fail(PKV_E_INVAL, "unknown sequence id");
     if ((int64_t)it->second.table.size() > max_blocks)
       return fail(PKV_E_INVAL, "table longer than max_blocks");
-    ptrs[i] = &it->second;
+    p->batch[i] = &it->second;
   }
   for (int32_t i = 0; i < n; ++i) {
-    const auto& t = ptrs[i]->table;
+    const auto& t = p->batch[i]->table;
     int32_t* row = tables_out + (int64_t)i * max_blocks;
     std::copy(t.begin(), t.end(), row);
     std::fill(row + t.size(), row + max_blocks, -1);
-    lens_out[i] = (int32_t)ptrs[i]->len;
+    lens_out[i] = (int32_t)p->batch[i]->len;
   }
   return PKV_OK;
+  PKV_GUARD_END
 }
 
 }  // extern "C"

@@ -14,6 +14,7 @@ namespace pkv {
 struct Sequence {
   std::vector<int32_t> table;  // logical block i -> physical block id
   int64_t len = 0;             // tokens stored
+  uint64_t mark = 0;           // batch calls: set to the call's stamp when seen
 };
 
 }  // namespace pkv
@@ -27,6 +28,12 @@ struct kv_pool {
   std::vector<int32_t> refcount;
   std::unordered_map<int32_t, pkv::Sequence> seqs;
   int32_t next_id = 0;
+  // scratch of the batch calls, kept between calls so that a steady decode
+  // loop allocates nothing on the host
+  mutable uint64_t stamp = 0;
+  mutable std::vector<pkv::Sequence*> batch;
+  std::vector<int32_t> ref_delta;    // [num_blocks], all 0 between calls
+  std::vector<int32_t> touched;      // blocks whose ref_delta is nonzero
 };
 
 namespace pkv {

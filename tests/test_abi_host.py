@@ -283,3 +283,18 @@ def test_decode_args_keep_their_tensors_alive():
     del a
     gc.collect()
     assert all(r() is None for r in refs)
+
+
+def test_metadata_upload_rejects_bad_arguments_on_host():
+    # null and misaligned arguments are refused before any HIP call
+    with pytest.raises(P.PagedKVError):
+        P.kv_metadata_upload(0, 4096, 16, 0)
+    with pytest.raises(P.PagedKVError):
+        P.kv_metadata_upload(4096, 0, 16, 0)
+    with pytest.raises(P.PagedKVError):
+        P.kv_metadata_upload(4096 + 4, 8192, 16, 0)
+    with pytest.raises(P.PagedKVError):
+        P.kv_metadata_upload(4096, 8192 + 4, 16, 0)
+    with pytest.raises(P.PagedKVError):
+        P.kv_metadata_upload(4096, 8192, 18, 0)
+    P.kv_metadata_upload(4096, 8192, 0, 0)   # nothing to copy: no-op
