@@ -286,6 +286,20 @@ pkv_status paged_attention_workspace_size(const kv_pool* pool, const paged_decod
 pkv_status paged_attention_decode(const kv_pool* pool, const paged_decode_args* args,
                                   pkv_stream stream);
 
+/* paged_attention_decode, timed by its own kernels (same operation, same
+ * pages).  kernel_events: host array of four hipEvent_t created with timing
+ * enabled (caller-owned): [0] and [1] are recorded when the attention kernel
+ * starts and ends, [2] and [3] when the log-sum-exp merge kernel starts and
+ * ends (hipExtLaunchKernelGGL), so each elapsed time is one kernel's
+ * duration on the device.  *n_kernels_out (may be NULL): 1 when the call ran
+ * no merge kernel (then [2] and [3] are left as they were), else 2.
+ * PKV_E_INVAL if kernel_events or one of its entries is NULL.  Recording an
+ * event makes the runtime finish the kernel with a system-scope release, which
+ * adds a few microseconds of idle time after it: time a sample of calls. */
+pkv_status paged_attention_decode_timed(const kv_pool* pool, const paged_decode_args* args,
+                                        pkv_stream stream, void* const* kernel_events,
+                                        int32_t* n_kernels_out);
+
 /* Message describing the last failure on the calling thread ("" if none). */
 const char* pkv_last_error(void);
 

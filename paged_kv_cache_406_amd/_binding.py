@@ -93,6 +93,8 @@ _SIGS = {
     "paged_kv_append": (c_i32, [P_pool, c_i32, c_vp, c_vp, c_i32, c_vp, c_i32, c_vp]),
     "paged_attention_workspace_size": (c_i32, [P_pool, ctypes.POINTER(paged_decode_args), ctypes.POINTER(c_size)]),
     "paged_attention_decode": (c_i32, [P_pool, ctypes.POINTER(paged_decode_args), c_vp]),
+    "paged_attention_decode_timed": (c_i32, [P_pool, ctypes.POINTER(paged_decode_args), c_vp,
+                                             ctypes.POINTER(c_vp), P_i32]),
     "pkv_last_error": (ctypes.c_char_p, []),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -328,3 +330,23 @@ def paged_attention_workspace_size(pool, args) -> int:
 
 def paged_attention_decode(pool, args, stream=None) -> None:
     _check(_lib.paged_attention_decode(pool, ctypes.byref(args), _stream(stream)))
+
+
+def paged_attention_decode_timed(pool, args, kernel_events, stream=None) -> int:
+    """paged_attention_decode with four events recorded by its kernels:
+    (attention start, attention end, merge start, merge end).  The events are
+    torch.cuda.Event(enable_timing=True) objects that have been recorded once
+    (torch creates the HIP event lazily), or raw hipEvent_t addresses.
+    Returns the number of kernels launched (1: no merge kernel)."""
+    hs = []
+    for e in kernel_events:
+        h = e if isinstance(e, int) else e.cuda_event
+        if not h:
+            raise ValueError("record each torch event once before passing it (its HIP event is created lazily)")
+        hs.append(h)
+    if len(hs) != 4:
+        raise ValueError("kernel_events needs four events")
+    arr = (c_vp * 4)(*hs)
+    nk = c_i32()
+    _check(_lib.paged_attention_decode_timed(pool, ctypes.byref(args), _stream(stream), arr, ctypes.byref(nk)))
+    return nk.value

@@ -45,6 +45,7 @@
 //    (unnormalised o, max, sum) and counted, and the wavefront that finishes
 //    the last piece of that sequence merges them.  Workgroups are remapped so
 //    that each XCD (one L2) gets a contiguous run of ranges.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -630,106 +631,75 @@ struct Decoder {
     }
   }
 
-  // One (KV head g, sequence b) piece: units [j0, j1) of its attended range.
-  // full: the piece is the whole range -> write the final output; otherwise
-  // write the partial (unnormalised o, max, sum) to workspace slot (w, which)
-  // for merge_kernel.
-  static __device__ void piece(const DecodeParams& P, int b, int g, int j0, int j1, bool full, int64_t w,
-                               int which) {
-    const int lane = threadIdx.x & 63;
-    const int i = lane & 15;
-    const int kg = lane >> 4;
-    int32_t L, lo, first, nu;
-    seq_extent<BS, U>(P, b, &L, &lo, &first, &nu);
-    L = uniform(L);
-    lo = uniform(lo);
-    first = uniform(first);
+  // A (KV head, sequence) pair with keys to attend.  All fields uniform.
+  struct Seg {
+    int32_t g, b;
+    int32_t L, lo, first;  // tokens, first attended key, its block
+    int32_t nb;            // work units of the pair
+    int64_t start;         // global index of the pair's first unit (range mode)
+  };
 
-    qop qo[NQ];
-    load_q(P, b, g, i, kg, qo);
-
-    State st;
-#pragma unroll
-    for (int n = 0; n < NV; ++n) st.O[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    st.m = -INFINITY;
-    st.l = 0.f;
-
-    // block-table entries of the piece, 64 at a time (one per lane), the next
-    // 64 loaded ahead
-    const int32_t* trow = P.tables + (int64_t)b * P.max_blocks;
-    const int32_t nblk_seq = (L + BS - 1) / BS;
-    const int32_t tb0 = first + j0 * UB;
-    const int32_t tb1 = min(first + j1 * UB, nblk_seq);
-    auto chunk = [&](int c) -> int32_t {
-      const int32_t idx = tb0 + 64 * c + lane;
-      return idx < tb1 ? trow[idx] : -1;
-    };
-    int32_t tcur = chunk(0);
-    int32_t tnext = tb1 - tb0 > 64 ? chunk(1) : -1;
-    int cur = 0;
-
-    auto where = [&](int s) -> Addr {
-      const int u = s / SPU;
-      const int sub = s % SPU;
-      const int rel = u * UB;
-      const int c = rel >> 6;
-      if (c != cur) {
-        tcur = tnext;
-        tnext = tb0 + 64 * (c + 1) < tb1 ? chunk(c + 1) : -1;
-        cur = c;
-      }
-      int32_t ids[UB];
-#pragma unroll
-      for (int k = 0; k < UB; ++k) ids[k] = __builtin_amdgcn_readlane(tcur, (rel & 63) + k);
-      return locate(P, g, ids, sub, (tb0 + rel) * BS + sub * TT, i, kg);
-    };
-
-    // Staggered pipeline over sub-tiles: the K loads of sub-tile s+1 are in
-    // flight while s is scored, its V loads while s is accumulated.
-    const int nsub = (j1 - j0) * SPU;
-    KTile K0, K1;
-    VTile V0, V1;
-    f32x4 S[NQT];
-    float p[NQT][4];
-    Addr a0 = where(0), a1;
-    load_k(K0, a0);
-    load_v(V0, a0);
-    // sched_barrier keeps the compiler from hoisting the next sub-tile's
-    // loads above the current one's math (that would hold three half-tiles
-    // at once and spill).
-    for (int s = 0; s < nsub; s += 2) {
-      const bool n1 = s + 1 < nsub;
-      if (n1) {
-        a1 = where(s + 1);
-        load_k(K1, a1);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      qk(K0, qo, S);
-      softmax(V0, S, st, p, lo, L, P.scale_log2, kg);
-      __builtin_amdgcn_sched_barrier(0);
-      if (n1) load_v(V1, a1);
-      __builtin_amdgcn_sched_barrier(0);
-      pv(V0, p, st, lo, L, kg);
-      __builtin_amdgcn_sched_barrier(0);
-      if (!n1) break;
-      const bool n2 = s + 2 < nsub;
-      if (n2) {
-        a0 = where(s + 2);
-        load_k(K0, a0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      qk(K1, qo, S);
-      softmax(V1, S, st, p, lo, L, P.scale_log2, kg);
-      __builtin_amdgcn_sched_barrier(0);
-      if (n2) load_v(V0, a0);
-      __builtin_amdgcn_sched_barrier(0);
-      pv(V1, p, st, lo, L, kg);
-      __builtin_amdgcn_sched_barrier(0);
+  static __device__ __forceinline__ Seg make_seg(const DecodeParams& P, const int32_t* C, int64_t t_head, int g,
+                                                 int b) {
+    Seg s;
+    int32_t nu;
+    seq_extent<BS, U>(P, b, &s.L, &s.lo, &s.first, &nu);
+    s.g = g;
+    s.b = b;
+    s.L = uniform(s.L);
+    s.lo = uniform(s.lo);
+    s.first = uniform(s.first);
+    if (C) {
+      const int32_t cb = uniform(C[b]);
+      s.nb = uniform(C[b + 1]) - cb;
+      s.start = (int64_t)g * t_head + cb;
+    } else {
+      s.nb = uniform(nu);
+      s.start = 0;
     }
+    return s;
+  }
 
+  // The next pair after s that has units; false past the last KV head.
+  static __device__ __forceinline__ bool next_seg(const DecodeParams& P, const int32_t* C, int64_t t_head,
+                                                  const Seg& s, Seg& out) {
+    int g = s.g, b = s.b;
+    do {
+      if (++b == P.batch) {
+        b = 0;
+        if (++g == P.hkv) return false;
+      }
+    } while (uniform(C[b + 1]) == uniform(C[b]));
+    out = make_seg(P, C, t_head, g, b);
+    return true;
+  }
+
+  // Entries [tb0 + 64c, tb0 + 64c + 64) of row b of the block tables, one
+  // per lane (-1 from tb1 on).
+  static __device__ __forceinline__ int32_t table_chunk(const DecodeParams& P, int b, int32_t tb0, int32_t tb1,
+                                                        int c, int lane) {
+    const int32_t idx = tb0 + 64 * c + lane;
+    return idx < tb1 ? P.tables[(int64_t)b * P.max_blocks + idx] : -1;
+  }
+
+  // Units [beg, end) of pair s (global unit indices) -> its block-table range.
+  static __device__ __forceinline__ void piece_blocks(const Seg& s, int64_t beg, int64_t end, int32_t* tb0,
+                                                      int32_t* tb1) {
+    const int32_t nblk = (s.L + BS - 1) / BS;
+    *tb0 = s.first + (int32_t)(beg - s.start) * UB;
+    *tb1 = min(s.first + (int32_t)(end - s.start) * UB, nblk);
+  }
+
+  // Final output or partial of the piece: units [beg, end) of pair s.  A
+  // piece that is the whole pair writes the output rows; otherwise the
+  // unnormalised o, max and sum go to workspace slot (w, which) for
+  // merge_kernel, and the range holding the pair's first unit writes the
+  // pair's merge job.
+  static __device__ __forceinline__ void finish(const DecodeParams& P, const State& st, const Seg& s, int64_t beg,
+                                                int64_t end, int64_t r0, int64_t T, int64_t W, int64_t w, int i,
+                                                int kg, int lane) {
     const float l1 = st.l + __shfl_xor(st.l, 16);
     const float lall = l1 + __shfl_xor(l1, 32);
-
     // FP8: the per-channel V scale, applied once to the output
     float vsc[NV][4];
 #pragma unroll
@@ -737,7 +707,7 @@ struct Decoder {
 #pragma unroll
       for (int r = 0; r < 4; ++r) vsc[n][r] = 1.0f;
     if constexpr (KV == KV_FP8) {
-      const float* vs = P.v_scale + ((int64_t)P.layer * P.hkv + g) * D;
+      const float* vs = P.v_scale + ((int64_t)P.layer * P.hkv + s.g) * D;
 #pragma unroll
       for (int n = 0; n < NV; ++n) {
         const f32x4 sc = *reinterpret_cast<const f32x4*>(vs + 16 * n + 4 * kg);
@@ -746,10 +716,12 @@ struct Decoder {
       }
     }
     const int G = P.group;
+    const bool full = beg == s.start && end == s.start + s.nb;
     if (full) {
+      if (!P.single && lane == 0) P.ws_job[(int64_t)s.g * P.batch + s.b] = make_int4(0, 0, 0, 0);
       if (i >= G) return;
       const float inv = lall > 0.f ? 1.0f / lall : 0.f;
-      const int64_t row = ((int64_t)b * P.hq + (int64_t)g * G + i) * D;
+      const int64_t row = ((int64_t)s.b * P.hq + (int64_t)s.g * G + i) * D;
 #pragma unroll
       for (int n = 0; n < NV; ++n) {
         f32x4 o;
@@ -758,6 +730,12 @@ struct Decoder {
         store4(P, row + 16 * n + 4 * kg, o);
       }
       return;
+    }
+    const int which = beg == r0 ? 0 : 1;
+    if (beg == s.start && lane == 0) {
+      const int64_t last = s.start + s.nb - 1;
+      P.ws_job[(int64_t)s.g * P.batch + s.b] =
+          make_int4((int)w, (int)(wave_of(last, T, W) - w + 1), which, 0);
     }
     if (i < G) {
       const int64_t slot = (w * 2 + which) * G + i;
@@ -772,10 +750,156 @@ struct Decoder {
       if (kg == 0) *reinterpret_cast<f32x2*>(P.ws_ml + slot * 2) = f32x2{st.m, lall};
     }
   }
+
+  // One wavefront's units [r0, r1) (KV-head-major global unit indices; the
+  // first lies in pair (g0, b0)) as one stream of sub-tiles: the loads run
+  // one sub-tile ahead of the math across piece boundaries, and the next
+  // piece's block-table entries and queries are fetched while the current
+  // piece streams.  C: unit prefix sums (NULL in single mode, where the range
+  // is the whole of one pair).
+  static __device__ void stream(const DecodeParams& P, const int32_t* C, int64_t t_head, int64_t T, int64_t W,
+                                int64_t w, int64_t r0, int64_t r1, int g0, int b0) {
+    const int lane = threadIdx.x & 63;
+    const int i = lane & 15;
+    const int kg = lane >> 4;
+
+    // load side: the piece whose sub-tiles are being fetched
+    Seg ls = make_seg(P, C, t_head, g0, b0);
+    if (!C) r1 = r0 + ls.nb;
+    int64_t lbeg = r0;
+    int64_t lend = min(r1, ls.start + ls.nb);
+    int32_t tb0, tb1;
+    piece_blocks(ls, lbeg, lend, &tb0, &tb1);
+    int32_t tcur = table_chunk(P, ls.b, tb0, tb1, 0, lane);
+    int32_t tnext = tb1 - tb0 > 64 ? table_chunk(P, ls.b, tb0, tb1, 1, lane) : -1;
+    int ccur = 0;
+    // the piece after it, with its first table entries in flight
+    Seg ln = ls;
+    bool has_ln = C && lend < r1 && next_seg(P, C, t_head, ls, ln);
+    int32_t tpn = -1;
+    if (has_ln) {
+      int32_t nb0, nb1;
+      piece_blocks(ln, ln.start, min(r1, ln.start + ln.nb), &nb0, &nb1);
+      tpn = table_chunk(P, ln.b, nb0, nb1, 0, lane);
+    }
+    qop q[NQ], qn[NQ];
+    load_q(P, ls.b, ls.g, i, kg, q);
+
+    // compute side: the piece whose sub-tiles are being scored
+    Seg cs = ls;
+    int64_t cbeg = lbeg, cend = lend;
+
+    int64_t lx = r0;  // unit and sub-tile of the next load
+    int lsub = 0;
+    auto where = [&](bool& last) -> Addr {
+      if (lx == lend) {
+        // enter the next piece
+        ls = ln;
+        lbeg = lend;
+        lend = min(r1, ls.start + ls.nb);
+        piece_blocks(ls, lbeg, lend, &tb0, &tb1);
+        tcur = tpn;
+        tnext = tb1 - tb0 > 64 ? table_chunk(P, ls.b, tb0, tb1, 1, lane) : -1;
+        ccur = 0;
+        load_q(P, ls.b, ls.g, i, kg, qn);
+        has_ln = lend < r1 && next_seg(P, C, t_head, ls, ln);
+        if (has_ln) {
+          int32_t nb0, nb1;
+          piece_blocks(ln, ln.start, min(r1, ln.start + ln.nb), &nb0, &nb1);
+          tpn = table_chunk(P, ln.b, nb0, nb1, 0, lane);
+        }
+      }
+      const int rel = (int)(lx - lbeg) * UB;
+      const int c = rel >> 6;
+      if (c != ccur) {
+        tcur = tnext;
+        tnext = tb0 + 64 * (c + 1) < tb1 ? table_chunk(P, ls.b, tb0, tb1, c + 1, lane) : -1;
+        ccur = c;
+      }
+      int32_t ids[UB];
+#pragma unroll
+      for (int k = 0; k < UB; ++k) ids[k] = __builtin_amdgcn_readlane(tcur, (rel & 63) + k);
+      const Addr a = locate(P, ls.g, ids, lsub, (tb0 + rel) * BS + lsub * TT, i, kg);
+      last = lsub == SPU - 1 && lx + 1 == lend;
+      if (++lsub == SPU) {
+        lsub = 0;
+        ++lx;
+      }
+      return a;
+    };
+
+    State st;
+    auto reset = [&]() {
+#pragma unroll
+      for (int n = 0; n < NV; ++n) st.O[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      st.m = -INFINITY;
+      st.l = 0.f;
+    };
+    reset();
+    // after the last sub-tile of a piece: write it, then take over the piece
+    // the loads have moved on to
+    auto step_piece = [&](bool more) {
+      finish(P, st, cs, cbeg, cend, r0, T, W, w, i, kg, lane);
+      if (more) {
+        cs = ls;
+        cbeg = lbeg;
+        cend = lend;
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) q[k] = qn[k];
+        reset();
+      }
+    };
+
+    // Staggered pipeline over sub-tiles: the K loads of sub-tile s+1 are in
+    // flight while s is scored, its V loads while s is accumulated.
+    const int64_t nsub = (r1 - r0) * SPU;
+    KTile K0, K1;
+    VTile V0, V1;
+    f32x4 S[NQT];
+    float p[NQT][4];
+    bool last0, last1;
+    Addr a0 = where(last0), a1;
+    load_k(K0, a0);
+    load_v(V0, a0);
+    // sched_barrier keeps the compiler from hoisting the next sub-tile's
+    // loads above the current one's math (that would hold three half-tiles
+    // at once and spill).
+    for (int64_t s = 0; s < nsub; s += 2) {
+      const bool n1 = s + 1 < nsub;
+      if (n1) {
+        a1 = where(last1);
+        load_k(K1, a1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      qk(K0, q, S);
+      softmax(V0, S, st, p, cs.lo, cs.L, P.scale_log2, kg);
+      __builtin_amdgcn_sched_barrier(0);
+      if (n1) load_v(V1, a1);
+      __builtin_amdgcn_sched_barrier(0);
+      pv(V0, p, st, cs.lo, cs.L, kg);
+      __builtin_amdgcn_sched_barrier(0);
+      if (last0) step_piece(n1);
+      if (!n1) break;
+      const bool n2 = s + 2 < nsub;
+      if (n2) {
+        a0 = where(last0);
+        load_k(K0, a0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      qk(K1, q, S);
+      softmax(V1, S, st, p, cs.lo, cs.L, P.scale_log2, kg);
+      __builtin_amdgcn_sched_barrier(0);
+      if (n2) load_v(V0, a0);
+      __builtin_amdgcn_sched_barrier(0);
+      pv(V1, p, st, cs.lo, cs.L, kg);
+      __builtin_amdgcn_sched_barrier(0);
+      if (last1) step_piece(n2);
+    }
+  }
 };
 
 template <int KV, int D, int BS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(DecodeParams P) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void decode_kernel(DecodeParams P) {
   typedef Decoder<KV, D, BS> Dec;
   constexpr int U = Units<KV, BS>::U;
   extern __shared__ int32_t C[];
@@ -796,7 +920,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
       write_zero_rows<D>(P, b, g, lane);
       return;
     }
-    Dec::piece(P, b, g, 0, nu, true, 0, 0);
+    Dec::stream(P, nullptr, 0, 0, 0, 0, 0, 0, g, b);
     return;
   }
 
@@ -820,47 +944,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   if (w < W) {
     const int64_t r0 = range_start(w, T, W);
     const int64_t r1 = range_start(w + 1, T, W);
-    int64_t x = r0;
-    while (x < r1) {
-      const int g = (int)(x / t_head);
-      const int32_t r = (int32_t)(x % t_head);
-      // largest b with C[b] <= r; the units of b are [C[b], C[b+1])
-      int lo_b = 0, hi_b = P.batch - 1;
-      while (lo_b < hi_b) {
-        const int mid = (lo_b + hi_b + 1) >> 1;
-        if (C[mid] <= r) lo_b = mid;
-        else hi_b = mid - 1;
-      }
-      const int b = uniform(lo_b);
-      const int32_t cb = uniform(C[b]);
-      const int32_t nb = uniform(C[b + 1]) - cb;
-      const int32_t j0 = r - cb;
-      const int64_t seg_start = x - j0;
-      const int64_t seg_end = seg_start + nb;
-      const int64_t pend = seg_end < r1 ? seg_end : r1;
-      const int32_t j1 = j0 + (int32_t)(pend - x);
-      const bool full = j0 == 0 && j1 == nb;
-      const int which = x == r0 ? 0 : 1;
-      Dec::piece(P, b, g, j0, j1, full, w, which);
-      // the range holding a sequence's first piece writes its merge job
-      if (j0 == 0 && lane == 0)
-        P.ws_job[(int64_t)g * P.batch + b] =
-            full ? make_int4(0, 0, 0, 0) : make_int4((int)w, (int)(wave_of(seg_end - 1, T, W) - w + 1), which, 0);
-      x = pend;
+    const int g = (int)(r0 / t_head);
+    const int32_t r = (int32_t)(r0 % t_head);
+    // largest b with C[b] <= r: the pair holding unit r0 (it has units)
+    int lo_b = 0, hi_b = P.batch - 1;
+    while (lo_b < hi_b) {
+      const int mid = (lo_b + hi_b + 1) >> 1;
+      if (C[mid] <= r) lo_b = mid;
+      else hi_b = mid - 1;
     }
+    Dec::stream(P, C, t_head, T, W, w, r0, r1, g, uniform(lo_b));
   }
 }
 
 // Log-sum-exp merge of the pieces of a split (KV head, sequence).  Workgroup
 // (seg, y) of 256 threads owns a contiguous share of the G * D/4 output
 // positions (head h, 4 dims) of sequence-head seg; TPP threads share a
-// position, thread sub taking pieces sub, sub + TPP, ...  Two passes with no
-// dependent chain: the max of the piece maxima (exact, order-free), then the
-// rescaled sums.  Lane-exchange butterflies leave the same bits in every lane
-// of a position (deterministic).  Piece p of a job whose first piece is in
-// range w0 is in slot (w0, first) for p = 0 and (w0 + p, 0) after.
+// position, thread sub taking pieces sub, sub + TPP, ...  Each thread loads
+// the (max, sum) and o of up to 8 of its pieces at once, so the partials are
+// read in one round trip after the job; more pieces are folded in batches of
+// 8 with the usual rescaling.  The thread maxima are combined by lane
+// exchanges, then the rescaled sums by a butterfly that leaves the same bits
+// in every lane of a position (deterministic).  Piece p of a job whose first
+// piece is in range w0 is in slot (w0, first) for p = 0 and (w0 + p, 0) after.
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeParams P) {
+  constexpr int NPC = 8;   // pieces per thread per batch
   const int64_t seg = blockIdx.x;
   const int4 job = P.ws_job[seg];
   const int npieces = job.y;
@@ -882,22 +991,44 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams P) {
     const int h = pos / D4;
     const int d4 = (pos % D4) * 4;
     auto slot = [&](int pc) -> int64_t { return ((w0 + pc) * 2 + (pc == 0 ? first_which : 0)) * G + h; };
-    float M = -INFINITY;
-#pragma unroll 8
-    for (int pc = sub; pc < npieces; pc += tpp) M = fmaxf(M, P.ws_ml[slot(pc) * 2]);
-    for (int off = 1; off < tpp; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
-    const float Mu = M == -INFINITY ? 0.f : M;
+    float M = -INFINITY, Ls = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float Ls = 0.f;
-#pragma unroll 8
-    for (int pc = sub; pc < npieces; pc += tpp) {
-      const int64_t sl = slot(pc);
-      const f32x2 ml = *reinterpret_cast<const f32x2*>(P.ws_ml + sl * 2);
-      const f32x4 o = *reinterpret_cast<const f32x4*>(P.ws_o + sl * D + d4);
-      const float wt = __builtin_amdgcn_exp2f(ml[0] - Mu);
-      acc += o * wt;
-      Ls += ml[1] * wt;
+    for (int base = sub; base < npieces; base += NPC * tpp) {
+      f32x2 ml[NPC];
+      f32x4 o[NPC];
+#pragma unroll
+      for (int k = 0; k < NPC; ++k) {
+        const int pc = base + k * tpp;
+        if (pc < npieces) {
+          const int64_t sl = slot(pc);
+          ml[k] = *reinterpret_cast<const f32x2*>(P.ws_ml + sl * 2);
+          o[k] = *reinterpret_cast<const f32x4*>(P.ws_o + sl * D + d4);
+        } else {
+          ml[k] = f32x2{-INFINITY, 0.f};
+          o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+      float Mb = M;
+#pragma unroll
+      for (int k = 0; k < NPC; ++k) Mb = fmaxf(Mb, ml[k][0]);
+      const float Mu = Mb == -INFINITY ? 0.f : Mb;
+      const float r = __builtin_amdgcn_exp2f(M - Mu);
+      acc *= r;
+      Ls *= r;
+#pragma unroll
+      for (int k = 0; k < NPC; ++k) {
+        const float wt = __builtin_amdgcn_exp2f(ml[k][0] - Mu);
+        acc += o[k] * wt;
+        Ls += ml[k][1] * wt;
+      }
+      M = Mb;
     }
+    // combine the tpp threads of the position: common max, rescale, sum
+    float Mall = M;
+    for (int off = 1; off < tpp; off <<= 1) Mall = fmaxf(Mall, __shfl_xor(Mall, off));
+    const float r = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mall);
+    acc *= r;
+    Ls *= r;
     for (int off = 1; off < tpp; off <<= 1) {
       Ls += __shfl_xor(Ls, off);
 #pragma unroll
@@ -1184,7 +1315,23 @@ pkv_status paged_attention_workspace_size(const kv_pool* pool, const paged_decod
   return PKV_OK;
 }
 
-pkv_status paged_attention_decode(const kv_pool* pool, const paged_decode_args* a, pkv_stream stream) {
+}  // extern "C"
+
+// Launch on s; start / stop (may be NULL) record when the first kernel
+// starts and the last one ends.
+template <typename K, typename... Args>
+static hipError_t launch(K kernel, dim3 grid, size_t lds, hipStream_t s, hipEvent_t start, hipEvent_t stop,
+                         Args... args) {
+  if (start || stop) hipExtLaunchKernelGGL(kernel, grid, dim3(256), (uint32_t)lds, s, start, stop, 0u, args...);
+  else hipLaunchKernelGGL(kernel, grid, dim3(256), lds, s, args...);
+  return hipGetLastError();
+}
+
+// ev: NULL or {attention start, attention end, merge start, merge end};
+// *nk: kernels launched.
+static pkv_status decode_launch(const kv_pool* pool, const paged_decode_args* a, pkv_stream stream,
+                                hipEvent_t const* ev, int32_t* nk) {
+  if (nk) *nk = 0;
   pkv_status st = check_decode(pool, a);
   if (st != PKV_OK) return st;
   if (a->batch == 0) return PKV_OK;
@@ -1221,9 +1368,10 @@ pkv_status paged_attention_decode(const kv_pool* pool, const paged_decode_args* 
     P.single = 1;
     P.num_waves = 0;
     const int64_t grid = (segs + 3) / 4;
-    hipLaunchKernelGGL(fn, dim3((uint32_t)grid), dim3(256), 0, s, P);
-    hipError_t e = hipGetLastError();
-    return e == hipSuccess ? PKV_OK : hip_fail(e, "decode launch");
+    hipError_t e = launch(fn, dim3((uint32_t)grid), 0, s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, P);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    if (nk) *nk = 1;
+    return PKV_OK;
   }
 
   int cus = 0;
@@ -1246,18 +1394,33 @@ pkv_status paged_attention_decode(const kv_pool* pool, const paged_decode_args* 
   grid = ((grid + 7) / 8) * 8;  // whole rounds over the 8 XCDs
   P.xcd_remap = 1;
   const size_t lds = (size_t)(a->batch + 1) * sizeof(int32_t);
-  hipLaunchKernelGGL(fn, dim3((uint32_t)grid), dim3(256), lds, s, P);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch(fn, dim3((uint32_t)grid), lds, s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, P);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
+  if (nk) *nk = 1;
   // few sequence-heads: spread each one's output positions over several
   // workgroups so that the merge still uses most CUs
   const int np = (int)(P.group * (d.head_dim / 4));
   int pg = 1;
   while (segs * pg < 512 && np / (pg * 2) >= 16) pg *= 2;
-  hipLaunchKernelGGL(d.head_dim == 64 ? merge_kernel<64> : merge_kernel<128>, dim3((uint32_t)segs, pg),
-                     dim3(256), 0, s, P);
-  e = hipGetLastError();
-  return e == hipSuccess ? PKV_OK : hip_fail(e, "merge launch");
+  e = launch(d.head_dim == 64 ? merge_kernel<64> : merge_kernel<128>, dim3((uint32_t)segs, pg), 0, s,
+             ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, P);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  if (nk) *nk = 2;
+  return PKV_OK;
+}
+
+extern "C" {
+
+pkv_status paged_attention_decode(const kv_pool* pool, const paged_decode_args* a, pkv_stream stream) {
+  return decode_launch(pool, a, stream, nullptr, nullptr);
+}
+
+pkv_status paged_attention_decode_timed(const kv_pool* pool, const paged_decode_args* a, pkv_stream stream,
+                                        void* const* kernel_events, int32_t* n_kernels_out) {
+  if (!kernel_events) return fail(PKV_E_INVAL, "kernel_events is NULL");
+  for (int k = 0; k < 4; ++k)
+    if (!kernel_events[k]) return fail(PKV_E_INVAL, "kernel_events needs four events");
+  return decode_launch(pool, a, stream, reinterpret_cast<hipEvent_t const*>(kernel_events), n_kernels_out);
 }
 
 }  // extern "C"

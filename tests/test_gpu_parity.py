@@ -316,3 +316,33 @@ def test_window_release_decodes_the_same(window):
             assert np.abs(got - ref).max() <= TOL[w.kv_dtype]
     finally:
         gst.close()
+
+
+@pytest.mark.parametrize("splits", [1, 0, 5])
+def test_timed_decode_matches_and_times(splits):
+    # paged_attention_decode_timed computes the same bits as
+    # paged_attention_decode; its kernel-recorded events give positive
+    # durations, for the merge kernel only when one ran
+    w, d, ost, gst = _state("gqa8_bf16")
+    tables, lens = ost.export()
+    q = wl.q_bits(w)
+    want = gst.decode(q, tables, lens, num_splits=splits)
+    qd, td, ld = to_dev(q), torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda()
+    out = torch.full((w.batch, w.num_q_heads, w.head_dim), -7.0, dtype=torch.float32, device="cuda")
+    a = P.make_decode_args(0, w.batch, w.num_q_heads, tables.shape[1], qd, w.q_dtype, td, ld,
+                           1.0 / math.sqrt(w.head_dim), out, num_splits=splits)
+    nbytes = P.paged_attention_workspace_size(gst.pool.handle, a)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+    a.workspace, a.workspace_bytes = ws.data_ptr(), nbytes
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        nk = P.paged_attention_decode_timed(gst.pool.handle, a, evs)
+        assert nk == (1 if splits == 1 else 2)
+        torch.cuda.synchronize()
+        assert evs[0].elapsed_time(evs[1]) > 0.0
+        if nk == 2:
+            assert evs[2].elapsed_time(evs[3]) > 0.0
+        assert np.array_equal(out.cpu().numpy().astype(np.float64), want)
