@@ -53,18 +53,24 @@ WORKLOAD_NAMES = {
 # HBM bytes per paged_attention_decode call (decode_kernel + merge_kernel, read +
 # write), from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs scaled by what the
 # same counters read for a plain 1 GiB device copy (FETCH x 2.0, WRITE x 1.0).
-# Each entry holds for the kernel source it was measured on (sha256 prefix of
-# csrc/kernels.hip); for any other source the figure is not reported.
+# Each entry holds for the kernel source it was measured on (kernels_sha());
+# for any other source the figure is not reported.
 MEASURED_TRAFFIC = {
-    "c3": (517.6e6, "9325eaef9d821ebe"),
+    "c3": (517.2e6, "487bf4b927966f99"),
+    "c5": (2158.7e6, "487bf4b927966f99"),
 }
 
 
 def kernels_sha():
+    """sha256 prefix of the device source the decode is built from (kernels.hip
+    and the headers beside it)."""
     import hashlib
-    path = os.path.join(ROOT, "paged_kv_cache_406_amd", "csrc", "kernels.hip")
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    csrc = os.path.join(ROOT, "paged_kv_cache_406_amd", "csrc")
+    h = hashlib.sha256()
+    for name in ["kernels.hip"] + sorted(f for f in os.listdir(csrc) if f.endswith(".h")):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
 
 
 def log(msg):

@@ -6,9 +6,10 @@
 //   copy_blocks_kernel whole-block copies for copy-on-write
 //   decode_kernel      decode attention over the paged cache: per-wavefront
 //                      ranges of (KV head, sequence, work unit), QK^T and PV
-//                      on MFMA, online softmax in registers, and the
-//                      log-sum-exp merge of sequences whose units were split
-//                      across wavefronts (done by the last piece to finish)
+//                      on MFMA, online softmax in registers; sequences whose
+//                      units straddle ranges leave partial results
+//   merge_kernel       log-sum-exp merge of those partial results
+//   upload_kernel      per-step metadata from page-locked host memory
 //
 // Pages followed: "AI 陪读顶会论文（三）：KV Cache 显存占用计算与 PagedAttention
 // 原理拆解" (section "为什么自回归解码…必须使用 KV Cache": the attention
@@ -40,10 +41,11 @@
 //    (two lane exchanges); sums stay per lane until the end.
 //  * Work split: the sub-tile-aligned units of all (KV head, sequence) pairs
 //    are laid end to end (KV-head major) and cut into W equal ranges, one per
-//    wavefront.  A range that covers a whole sequence writes the final
-//    output; a piece of a sequence that straddles ranges is written as
-//    (unnormalised o, max, sum) and counted, and the wavefront that finishes
-//    the last piece of that sequence merges them.  Workgroups are remapped so
+//    wavefront.  A wavefront streams its range as one sequence of sub-tiles,
+//    its loads one sub-tile ahead across the boundaries between sequences.
+//    A range that covers a whole sequence writes the final output; a piece
+//    of a sequence that straddles ranges is written as (unnormalised o, max,
+//    sum), and merge_kernel combines the pieces.  Workgroups are remapped so
 //    that each XCD (one L2) gets a contiguous run of ranges.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
