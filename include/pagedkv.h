@@ -191,6 +191,15 @@ pkv_status block_table_release_before(kv_pool* pool, int32_t seq, int32_t token,
 pkv_status block_table_get(const kv_pool* pool, int32_t seq, int32_t* blocks_out,
                            int32_t cap, int32_t* n_blocks_out, int32_t* len_out);
 
+/* Leading blocks shared by a batch: the largest k such that, for every
+ * sequence in seqs, table entries 0 .. k-1 are the same physical blocks as
+ * seqs[0]'s and all k blocks are full (k * block_size <= its length).  These
+ * are the blocks forked sequences still hold in common (page "生成一个字…",
+ * section "PagedAttention：…": a shared prefix is stored once, reference
+ * counted).  n == 0 gives 0.  PKV_E_INVAL for an unknown id. */
+pkv_status block_table_common_prefix(const kv_pool* pool, const int32_t* seqs, int32_t n,
+                                     int32_t* blocks_out);
+
 /* Dense export for the decode kernel: tables_out host int32 [n][max_blocks]
  * (row i = table of seqs[i], padded with -1), lens_out host int32 [n] (token
  * counts).  PKV_E_INVAL if a table has more than max_blocks entries. */
@@ -259,6 +268,22 @@ typedef struct {
   int32_t out_dtype;            /* PKV_F32 (recommended), PKV_F16 or PKV_BF16 */
   void* workspace;              /* device, caller-owned, 256-byte aligned */
   size_t workspace_bytes;       /* >= paged_attention_workspace_size() */
+  int32_t shared_prefix_blocks; /* 0: off.  k > 0: the first k table entries of
+                                   every row are the same physical blocks as row
+                                   0's (block_table_common_prefix gives the largest
+                                   such k).  Those blocks are then read once for
+                                   the whole batch by a prefix pass, which scores
+                                   every query of a KV head against each of their
+                                   K/V sub-tiles, and each sequence's own blocks
+                                   from k on are read as usual; the two are joined
+                                   by the log-sum-exp merge.  Same result as k = 0.
+                                   Needs sliding_window == 0 (else
+                                   PKV_E_UNSUPPORTED) and k <= max_blocks_per_seq;
+                                   the workspace is then needed for every
+                                   num_splits.  Page "生成一个字…", section
+                                   "PagedAttention：…", and page "AI 陪读顶会论文（三）",
+                                   innovation 3: a shared prefix is stored once;
+                                   here it is also read once per call. */
 } paged_decode_args;
 
 /* Workspace paged_attention_decode needs for these arguments (0 for a single
@@ -289,9 +314,10 @@ pkv_status paged_attention_decode(const kv_pool* pool, const paged_decode_args* 
 /* paged_attention_decode, timed by its own kernels (same operation, same
  * pages).  kernel_events: host array of four hipEvent_t created with timing
  * enabled (caller-owned): [0] and [1] are recorded when the attention kernel
- * starts and ends, [2] and [3] when the log-sum-exp merge kernel starts and
- * ends (hipExtLaunchKernelGGL), so each elapsed time is one kernel's
- * duration on the device.  *n_kernels_out (may be NULL): 1 when the call ran
+ * starts and ends (with a shared prefix, [0] when the prefix pass before it
+ * starts), [2] and [3] when the log-sum-exp merge kernel starts and ends
+ * (hipExtLaunchKernelGGL), so each elapsed time is the device duration of
+ * those kernels.  *n_kernels_out (may be NULL): 1 when the call ran
  * no merge kernel (then [2] and [3] are left as they were), else 2.
  * PKV_E_INVAL if kernel_events or one of its entries is NULL.  Recording an
  * event makes the runtime finish the kernel with a system-scope release, which

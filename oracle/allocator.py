@@ -217,6 +217,30 @@ class BlockManager:
             n += 1
         return n
 
+    # ---- shared prefix ----------------------------------------------------
+    def common_prefix(self, seqs) -> int:
+        """Number of leading logical blocks that every sequence in seqs holds
+        as the very same physical blocks as the first one, counting only
+        blocks that are full in all of them.  Forked sequences keep their
+        parent's blocks until they write into them (page "生成一个字…", section
+        "PagedAttention：…": a shared prefix is stored once and reference
+        counted), so this is the part of the family's cache that is stored
+        once."""
+        seqs = [int(s) for s in seqs]
+        for s in seqs:
+            self._check(s)
+        if not seqs:
+            return 0
+        first = self._tables[seqs[0]]
+        k = 0
+        while k < len(first) and first[k] >= 0:
+            same = all(len(self._tables[s]) > k and self._tables[s][k] == first[k] for s in seqs)
+            full = all((k + 1) * self.block_size <= self._lens[s] for s in seqs)
+            if not (same and full):
+                break
+            k += 1
+        return k
+
     # ---- dense export ----------------------------------------------------
     def export(self, seqs, max_blocks: int):
         """Dense int32 tables [n][max_blocks] padded with -1 and int32 lengths."""

@@ -65,7 +65,7 @@ class paged_decode_args(ctypes.Structure):
                 ("q", c_vp), ("q_dtype", c_i32),
                 ("block_tables", c_vp), ("context_lens", c_vp),
                 ("scale", c_float), ("out", c_vp), ("out_dtype", c_i32),
-                ("workspace", c_vp), ("workspace_bytes", c_size)]
+                ("workspace", c_vp), ("workspace_bytes", c_size), ("shared_prefix_blocks", c_i32)]
 
 
 P_pool = c_vp
@@ -88,6 +88,7 @@ _SIGS = {
     "block_table_release_before": (c_i32, [P_pool, c_i32, c_i32, P_i32]),
     "block_table_get": (c_i32, [P_pool, c_i32, P_i32, c_i32, P_i32, P_i32]),
     "block_table_export": (c_i32, [P_pool, c_vp, c_i32, c_i32, c_vp, c_vp]),
+    "block_table_common_prefix": (c_i32, [P_pool, c_vp, c_i32, P_i32]),
     "kv_pool_copy_blocks": (c_i32, [P_pool, c_vp, c_i32, c_vp]),
     "kv_metadata_upload": (c_i32, [c_vp, c_vp, c_size, c_vp]),
     "paged_kv_append": (c_i32, [P_pool, c_i32, c_vp, c_vp, c_i32, c_vp, c_i32, c_vp]),
@@ -288,6 +289,14 @@ def block_table_export(pool, seqs, max_blocks, tables_out=None, lens_out=None):
     return tables, lens
 
 
+def block_table_common_prefix(pool, seqs) -> int:
+    """Leading physical blocks, all full, that every sequence shares with seqs[0]."""
+    arr, arr_p = _i32_addr(seqs)
+    out = c_i32()
+    _check(_lib.block_table_common_prefix(pool, arr_p, len(arr), ctypes.byref(out)))
+    return out.value
+
+
 # ---- device work ------------------------------------------------------------
 def kv_pool_copy_blocks(pool, d_pairs, n, stream=None) -> None:
     _check(_lib.kv_pool_copy_blocks(pool, _ptr(d_pairs), n, _stream(stream)))
@@ -306,7 +315,7 @@ def paged_kv_append(pool, layer, d_k, d_v, src_dtype, d_slots, n_tokens, stream=
 
 def make_decode_args(layer, batch, num_q_heads, max_blocks_per_seq, q, q_dtype, block_tables,
                      context_lens, scale, out, out_dtype="f32", sliding_window=0, num_splits=0,
-                     workspace=None, workspace_bytes=0):
+                     workspace=None, workspace_bytes=0, shared_prefix_blocks=0):
     a = paged_decode_args()
     a.layer, a.batch, a.num_q_heads = layer, batch, num_q_heads
     a.max_blocks_per_seq, a.sliding_window, a.num_splits = max_blocks_per_seq, sliding_window, num_splits
@@ -315,6 +324,7 @@ def make_decode_args(layer, batch, num_q_heads, max_blocks_per_seq, q, q_dtype, 
     a.scale = scale
     a.out, a.out_dtype = _ptr(out), DTYPE_CODE.get(out_dtype, out_dtype)
     a.workspace, a.workspace_bytes = _ptr(workspace), workspace_bytes
+    a.shared_prefix_blocks = shared_prefix_blocks
     # the struct holds raw device addresses: keep the tensors they came from
     # alive as long as the struct, or torch may hand their memory to the next
     # allocation before the decode is launched

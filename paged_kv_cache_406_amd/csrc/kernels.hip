@@ -232,6 +232,13 @@ struct DecodeParams {
   int32_t single;     // 1: one wavefront per (KV head, sequence)
   int32_t xcd_remap;
   float scale_log2;   // scale * log2(e)
+  // shared prefix: the first `shared` table entries of every row are row 0's
+  // blocks; prefix_kernel leaves one partial (o[D], max, sum) per (chunk,
+  // sequence, query head) in ws_pre, and merge_kernel folds them in
+  int32_t shared;     // 0: off
+  int32_t pre_chunks; // token chunks of the prefix
+  int32_t pre_rtiles; // query-row tiles per KV head
+  float* ws_pre;      // [pre_chunks + 1][B * Hq][D + 4]: o, max, sum, 2 pad
 };
 
 // Tokens per sub-tile: the amount one wavefront loads and scores at a time.
@@ -259,11 +266,13 @@ __device__ __forceinline__ void seq_extent(const DecodeParams& P, int b, int32_t
   const int32_t cap = P.max_blocks * BS;
   L = L < 0 ? 0 : (L > cap ? cap : L);
   const int32_t lo = P.window > 0 ? (L - P.window > 0 ? L - P.window : 0) : 0;
-  const int32_t first = lo / BS;
+  // with a shared prefix (no window) the blocks before `shared` are
+  // prefix_kernel's
+  const int32_t first = P.shared > 0 ? P.shared : lo / BS;
   *L_out = L;
   *lo_out = lo;
   *first_out = first;
-  *nunits_out = L > lo ? (L - first * BS + U - 1) / U : 0;
+  *nunits_out = L > lo && L > first * BS ? (L - first * BS + U - 1) / U : 0;
 }
 
 // Exclusive prefix sums of the per-sequence unit counts into C[0..B] (LDS).
@@ -421,7 +430,13 @@ struct Decoder {
   static __device__ __forceinline__ void load_q(const DecodeParams& P, int b, int g, int i, int kg,
                                                 qop (&qo)[NQ]) {
     const bool live = i < P.group;
-    const int64_t row = ((int64_t)b * P.hq + (int64_t)g * P.group + (live ? i : 0)) * D;
+    load_q_at(P, g, ((int64_t)b * P.hq + (int64_t)g * P.group + (live ? i : 0)) * D, live, kg, qo);
+  }
+
+  // Query row (element offset `row` of q, a head of KV head g) as this lane's
+  // MFMA column; zeros when !live.
+  static __device__ __forceinline__ void load_q_at(const DecodeParams& P, int g, int64_t row, bool live, int kg,
+                                                   qop (&qo)[NQ]) {
     if constexpr (KV == KV_F32) {
       const float* q = reinterpret_cast<const float*>(P.q) + row;
 #pragma unroll
@@ -692,6 +707,26 @@ struct Decoder {
     *tb1 = min(s.first + (int32_t)(end - s.start) * UB, nblk);
   }
 
+  // FP8: the per-channel V scale of this lane's output channels (1 otherwise).
+  static __device__ __forceinline__ void v_scales(const DecodeParams& P, int g, int kg, float (&vsc)[NV][4]) {
+#pragma unroll
+    for (int n = 0; n < NV; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vsc[n][r] = 1.0f;
+    if constexpr (KV == KV_FP8) {
+      const float* vs = P.v_scale + ((int64_t)P.layer * P.hkv + g) * D;
+#pragma unroll
+      for (int n = 0; n < NV; ++n) {
+        const f32x4 sc = *reinterpret_cast<const f32x4*>(vs + 16 * n + 4 * kg);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vsc[n][r] = sc[r];
+      }
+    }
+  }
+
+  // Row stride (floats) of a prefix partial: o[D], max, sum, 2 pad (16-byte rows).
+  static constexpr int PRE_STRIDE = D + 4;
+
   // Final output or partial of the piece: units [beg, end) of pair s.  A
   // piece that is the whole pair writes the output rows; otherwise the
   // unnormalised o, max and sum go to workspace slot (w, which) for
@@ -704,21 +739,26 @@ struct Decoder {
     const float lall = l1 + __shfl_xor(l1, 32);
     // FP8: the per-channel V scale, applied once to the output
     float vsc[NV][4];
-#pragma unroll
-    for (int n = 0; n < NV; ++n)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) vsc[n][r] = 1.0f;
-    if constexpr (KV == KV_FP8) {
-      const float* vs = P.v_scale + ((int64_t)P.layer * P.hkv + s.g) * D;
-#pragma unroll
-      for (int n = 0; n < NV; ++n) {
-        const f32x4 sc = *reinterpret_cast<const f32x4*>(vs + 16 * n + 4 * kg);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) vsc[n][r] = sc[r];
-      }
-    }
+    v_scales(P, s.g, kg, vsc);
     const int G = P.group;
     const bool full = beg == s.start && end == s.start + s.nb;
+    if (full && P.shared) {
+      // the whole of the pair's own part: its partial goes to the slot after
+      // the prefix chunks, and merge_kernel joins the two (job.w = 1)
+      if (lane == 0) P.ws_job[(int64_t)s.g * P.batch + s.b] = make_int4(0, 0, 0, 1);
+      if (i >= G) return;
+      const int64_t hrow = (int64_t)s.b * P.hq + (int64_t)s.g * G + i;
+      float* base = P.ws_pre + ((int64_t)P.pre_chunks * P.batch * P.hq + hrow) * PRE_STRIDE;
+#pragma unroll
+      for (int n = 0; n < NV; ++n) {
+        f32x4 o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = st.O[n][r] * vsc[n][r];
+        *reinterpret_cast<f32x4*>(base + 16 * n + 4 * kg) = o;
+      }
+      if (kg == 0) *reinterpret_cast<f32x2*>(base + D) = f32x2{st.m, lall};
+      return;
+    }
     if (full) {
       if (!P.single && lane == 0) P.ws_job[(int64_t)s.g * P.batch + s.b] = make_int4(0, 0, 0, 0);
       if (i >= G) return;
@@ -750,6 +790,133 @@ struct Decoder {
         *reinterpret_cast<f32x4*>(wo + 16 * n + 4 * kg) = o;
       }
       if (kg == 0) *reinterpret_cast<f32x2*>(P.ws_ml + slot * 2) = f32x2{st.m, lall};
+    }
+  }
+
+  // Query-row tiles (MFMA column blocks of 16 rows) per wavefront of prefix_kernel.
+  static constexpr int NT = 2;
+
+  // Shared prefix, one wavefront: query rows rt*16*NT .. +16*NT of KV head g
+  // (row r = sequence r / G, head g*G + r % G) against token chunk c of the
+  // prefix (row 0's first `shared` blocks), every K/V sub-tile used for all of
+  // its rows.  Each row attends prefix tokens below min(its L, prefix).
+  // Writes the chunk's partial (o in output units, max, sum) of every row.
+  static __device__ void prefix_piece(const DecodeParams& P, int g, int rt, int c) {
+    const int lane = threadIdx.x & 63;
+    const int i = lane & 15;
+    const int kg = lane >> 4;
+    const int G = P.group;
+    const int64_t nrows = (int64_t)P.batch * G;
+    const int32_t kT = P.shared * BS;
+    const int32_t cap = P.max_blocks * BS;
+    qop q[NT][NQ];
+    State st[NT];
+    int32_t Lc[NT];
+    int64_t hrow[NT];
+    bool live[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int64_t r = (int64_t)rt * 16 * NT + t * 16 + i;
+      live[t] = r < nrows;
+      const int b = live[t] ? (int)(r / G) : 0;
+      const int hg = live[t] ? (int)(r % G) : 0;
+      hrow[t] = (int64_t)b * P.hq + (int64_t)g * G + hg;
+      load_q_at(P, g, hrow[t] * D, live[t], kg, q[t]);
+      int32_t L = P.lens[b];
+      L = L < 0 ? 0 : (L > cap ? cap : L);
+      Lc[t] = live[t] ? min(L, kT) : 0;
+#pragma unroll
+      for (int n = 0; n < NV; ++n) st[t].O[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      st[t].m = -INFINITY;
+      st[t].l = 0.f;
+    }
+    const int32_t nsp = (kT + TT - 1) / TT;
+    const int32_t s0 = (int32_t)((int64_t)c * nsp / P.pre_chunks);
+    const int32_t s1 = (int32_t)((int64_t)(c + 1) * nsp / P.pre_chunks);
+
+    // row 0's table entries of the prefix, 64 at a time, one per lane
+    int ccur = -1;
+    int32_t tcur = -1;
+    auto where = [&](int32_t s) -> Addr {
+      const int32_t tok = s * TT;
+      const int32_t rel = (tok / U) * UB;  // first table entry of the unit
+      const int cc = rel >> 6;
+      if (cc != ccur) {
+        tcur = table_chunk(P, 0, 0, P.shared, cc, lane);
+        ccur = cc;
+      }
+      int32_t ids[UB];
+#pragma unroll
+      for (int k = 0; k < UB; ++k) ids[k] = __builtin_amdgcn_readlane(tcur, (rel & 63) + k);
+      return locate(P, g, ids, (tok % U) / TT, tok, i, kg);
+    };
+
+    if (s0 < s1) {
+      KTile K0, K1;
+      VTile V0, V1;
+      f32x4 S[NQT];
+      float pp[NT][NQT][4];
+      Addr a0 = where(s0), a1;
+      load_k(K0, a0);
+      load_v(V0, a0);
+      // the staggered two-buffer pipeline of stream(), each sub-tile scored
+      // and accumulated for all NT row tiles
+      for (int32_t s = s0; s < s1; s += 2) {
+        const bool n1 = s + 1 < s1;
+        if (n1) {
+          a1 = where(s + 1);
+          load_k(K1, a1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          qk(K0, q[t], S);
+          softmax(V0, S, st[t], pp[t], 0, Lc[t], P.scale_log2, kg);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (n1) load_v(V1, a1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) pv(V0, pp[t], st[t], 0, kT, kg);
+        __builtin_amdgcn_sched_barrier(0);
+        if (!n1) break;
+        const bool n2 = s + 2 < s1;
+        if (n2) {
+          a0 = where(s + 2);
+          load_k(K0, a0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          qk(K1, q[t], S);
+          softmax(V1, S, st[t], pp[t], 0, Lc[t], P.scale_log2, kg);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (n2) load_v(V0, a0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) pv(V1, pp[t], st[t], 0, kT, kg);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    float vsc[NV][4];
+    v_scales(P, g, kg, vsc);
+    const int64_t bhq = (int64_t)P.batch * P.hq;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float l1 = st[t].l + __shfl_xor(st[t].l, 16);
+      const float lall = l1 + __shfl_xor(l1, 32);
+      if (!live[t]) continue;
+      float* base = P.ws_pre + ((int64_t)c * bhq + hrow[t]) * PRE_STRIDE;
+#pragma unroll
+      for (int n = 0; n < NV; ++n) {
+        f32x4 o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = st[t].O[n][r] * vsc[n][r];
+        *reinterpret_cast<f32x4*>(base + 16 * n + 4 * kg) = o;
+      }
+      if (kg == 0) *reinterpret_cast<f32x2*>(base + D) = f32x2{st[t].m, lall};
     }
   }
 
@@ -935,7 +1102,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int64_t seg = w; seg < nseg; seg += launched) {
     const int b = (int)(seg % P.batch);
     if (C[b + 1] == C[b]) {
-      write_zero_rows<D>(P, b, (int)(seg / P.batch), lane);
+      // nothing of its own to attend: zeros, or (shared prefix) the merge of
+      // the prefix partials alone, written by merge_kernel
+      if (!P.shared) write_zero_rows<D>(P, b, (int)(seg / P.batch), lane);
       if (lane == 0) P.ws_job[seg] = make_int4(0, 0, 0, 0);
     }
   }
@@ -959,6 +1128,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 }
 
+// Shared prefix: wavefront w takes (KV head g, query-row tile rt, token
+// chunk c), KV-head major, so the ranges of one head sit on one XCD and its
+// prefix blocks stay in that XCD's L2.
+template <int KV, int D, int BS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefix_kernel(DecodeParams P) {
+  typedef Decoder<KV, D, BS> Dec;
+  const int wid = uniform((int)(threadIdx.x >> 6));
+  int64_t wg = blockIdx.x;
+  wg = (wg % 8) * (gridDim.x / 8) + wg / 8;
+  const int64_t w = wg * 4 + wid;
+  const int64_t per_head = (int64_t)P.pre_rtiles * P.pre_chunks;
+  if (w >= per_head * P.hkv) return;
+  const int g = uniform((int)(w / per_head));
+  const int64_t rem = w % per_head;
+  Dec::prefix_piece(P, g, uniform((int)(rem / P.pre_chunks)), uniform((int)(rem % P.pre_chunks)));
+}
+
 // Log-sum-exp merge of the pieces of a split (KV head, sequence).  Workgroup
 // (seg, y) of 256 threads owns a contiguous share of the G * D/4 output
 // positions (head h, 4 dims) of sequence-head seg; TPP threads share a
@@ -975,7 +1161,7 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams P) {
   const int64_t seg = blockIdx.x;
   const int4 job = P.ws_job[seg];
   const int npieces = job.y;
-  if (npieces == 0) return;
+  if (npieces == 0 && !P.shared) return;
   const int64_t w0 = job.x;
   const int first_which = job.z;
   const int b = (int)(seg % P.batch), g = (int)(seg / P.batch);
@@ -1024,6 +1210,24 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams P) {
         Ls += ml[k][1] * wt;
       }
       M = Mb;
+    }
+    // the prefix partials of this (sequence, head), and (job.w) the partial
+    // of its own part when one wavefront held all of it: same fold
+    if (P.shared) {
+      const int64_t bhq = (int64_t)P.batch * P.hq;
+      const int64_t hrow = (int64_t)b * P.hq + (int64_t)g * G + h;
+      const int nslots = P.pre_chunks + (job.w ? 1 : 0);
+      for (int cc = sub; cc < nslots; cc += tpp) {
+        const float* base = P.ws_pre + ((int64_t)cc * bhq + hrow) * (D + 4);
+        const float mc = base[D];
+        const float Mb = fmaxf(M, mc);
+        const float Mu = Mb == -INFINITY ? 0.f : Mb;
+        const float r = __builtin_amdgcn_exp2f(M - Mu);
+        const float wt = __builtin_amdgcn_exp2f(mc - Mu);
+        acc = acc * r + *reinterpret_cast<const f32x4*>(base + d4) * wt;
+        Ls = Ls * r + base[D + 1] * wt;
+        M = Mb;
+      }
     }
     // combine the tpp threads of the position: common max, rescale, sum
     float Mall = M;
@@ -1129,29 +1333,63 @@ static pkv_status check_decode(const kv_pool* pool, const paged_decode_args* a) 
     return fail(PKV_E_INVAL, "null device pointer");
   if ((reinterpret_cast<uintptr_t>(a->q) | reinterpret_cast<uintptr_t>(a->out)) % 16)
     return fail(PKV_E_INVAL, "q and out must be 16-byte aligned");
+  if (a->shared_prefix_blocks < 0 || a->shared_prefix_blocks > a->max_blocks_per_seq)
+    return fail(PKV_E_INVAL, "shared_prefix_blocks must lie in [0, max_blocks_per_seq]");
+  if (a->shared_prefix_blocks > 0 && a->sliding_window > 0)
+    return fail(PKV_E_UNSUPPORTED, "a shared prefix with a sliding window is not supported");
   return PKV_OK;
+}
+
+static int tokens_per_subtile(int kv) {
+  return kv == PKV_F32 ? SubTile<KV_F32>::TT : (kv == PKV_FP8_E4M3 ? SubTile<KV_FP8>::TT : SubTile<KV_BF16>::TT);
+}
+
+// Shared prefix work split: query-row tiles per KV head and token chunks,
+// about two wavefronts per CU in all, at most 16 chunks.
+static void prefix_plan(const kv_pool* pool, const paged_decode_args* a, int cus, int32_t* rtiles,
+                        int32_t* chunks) {
+  const kv_pool_desc& d = pool->desc;
+  constexpr int rows_per_wave = 16 * Decoder<KV_BF16, 128, 16>::NT;
+  const int64_t G = a->num_q_heads / d.num_kv_heads;
+  const int64_t rt = ((int64_t)a->batch * G + rows_per_wave - 1) / rows_per_wave;
+  const int64_t tt = tokens_per_subtile(d.kv_dtype);
+  const int64_t nsp = ((int64_t)a->shared_prefix_blocks * d.block_size + tt - 1) / tt;
+  int64_t c = (2 * (int64_t)cus) / std::max<int64_t>(1, d.num_kv_heads * rt);
+  c = std::max<int64_t>(1, std::min<int64_t>({c, nsp, 16}));
+  *rtiles = (int32_t)rt;
+  *chunks = (int32_t)c;
 }
 
 static int64_t num_waves_for(const paged_decode_args* a, int cus) {
   return a->num_splits >= 2 ? (int64_t)a->num_splits : (int64_t)cus * kWavesPerCU;
 }
 
+
 // Workspace: merge jobs [Hkv][B] int4, partial outputs [W][2][G][D] fp32
-// and partial (max, sum) [W][2][G][2] fp32, each part 256-byte aligned.
-// Every call writes each job record before merge_kernel reads it, so the
-// workspace needs no initialisation.
+// and partial (max, sum) [W][2][G][2] fp32 (range mode only), then the
+// shared-prefix partials [chunks + 1][B * Hq][D + 4] fp32 (with a shared
+// prefix; the last slot holds the own part of pairs that one wavefront held
+// whole), each part 256-byte aligned.
 struct WsLayout {
-  size_t job_off, o_off, ml_off, total;
+  size_t job_off, o_off, ml_off, pre_off, total;
 };
 
-static WsLayout workspace_layout(const kv_pool* pool, const paged_decode_args* a, int64_t W) {
+static WsLayout workspace_layout(const kv_pool* pool, const paged_decode_args* a, int64_t W, bool single,
+                                 int32_t pre_chunks) {
   const int64_t G = a->num_q_heads / pool->desc.num_kv_heads;
   auto up = [](size_t x) { return ((x + 255) / 256) * 256; };
   WsLayout l;
-  l.job_off = 0;
-  l.o_off = up((size_t)pool->desc.num_kv_heads * a->batch * sizeof(int4));
-  l.ml_off = l.o_off + up((size_t)W * 2 * G * pool->desc.head_dim * sizeof(float));
-  l.total = l.ml_off + up((size_t)W * 2 * G * 2 * sizeof(float));
+  l.job_off = l.o_off = l.ml_off = 0;
+  size_t end = 0;
+  if (!single) {
+    l.o_off = up((size_t)pool->desc.num_kv_heads * a->batch * sizeof(int4));
+    l.ml_off = l.o_off + up((size_t)W * 2 * G * pool->desc.head_dim * sizeof(float));
+    end = l.ml_off + up((size_t)W * 2 * G * 2 * sizeof(float));
+  }
+  l.pre_off = end;
+  if (a->shared_prefix_blocks > 0)
+    end += up((size_t)(pre_chunks + 1) * a->batch * a->num_q_heads * (pool->desc.head_dim + 4) * sizeof(float));
+  l.total = end;
   return l;
 }
 
@@ -1179,6 +1417,27 @@ static decode_fn pick_decode(int kv, int d, int bs) {
     case PKV_F16: return pick_decode_d<KV_F16>(d, bs);
     case PKV_BF16: return pick_decode_d<KV_BF16>(d, bs);
     case PKV_FP8_E4M3: return pick_decode_d<KV_FP8>(d, bs);
+  }
+  return nullptr;
+}
+
+template <int KV, int D>
+static decode_fn pick_prefix_bs(int bs) {
+  switch (bs) {
+    case 16: return prefix_kernel<KV, D, 16>;
+    case 32: return prefix_kernel<KV, D, 32>;
+    case 64: return prefix_kernel<KV, D, 64>;
+    case 128: return prefix_kernel<KV, D, 128>;
+  }
+  return nullptr;
+}
+
+static decode_fn pick_prefix(int kv, int d, int bs) {
+  switch (kv) {
+    case PKV_F32: return d == 64 ? pick_prefix_bs<KV_F32, 64>(bs) : pick_prefix_bs<KV_F32, 128>(bs);
+    case PKV_F16: return d == 64 ? pick_prefix_bs<KV_F16, 64>(bs) : pick_prefix_bs<KV_F16, 128>(bs);
+    case PKV_BF16: return d == 64 ? pick_prefix_bs<KV_BF16, 64>(bs) : pick_prefix_bs<KV_BF16, 128>(bs);
+    case PKV_FP8_E4M3: return d == 64 ? pick_prefix_bs<KV_FP8, 64>(bs) : pick_prefix_bs<KV_FP8, 128>(bs);
   }
   return nullptr;
 }
@@ -1304,16 +1563,15 @@ pkv_status paged_attention_workspace_size(const kv_pool* pool, const paged_decod
   if (!bytes_out) return fail(PKV_E_INVAL, "null argument");
   pkv_status st = check_decode(pool, a);
   if (st != PKV_OK) return st;
-  if (a->num_splits == 1) {
-    *bytes_out = 0;
-    return PKV_OK;
-  }
+  const bool single = a->shared_prefix_blocks == 0 && (a->num_splits == 1 || a->max_blocks_per_seq == 0);
   int cus = 0;
-  if (a->num_splits == 0) {
+  if ((!single && a->num_splits <= 1) || a->shared_prefix_blocks > 0) {
     st = device_cus(&cus);
     if (st != PKV_OK) return st;
   }
-  *bytes_out = workspace_layout(pool, a, num_waves_for(a, cus)).total;
+  int32_t rtiles = 0, chunks = 0;
+  if (a->shared_prefix_blocks > 0) prefix_plan(pool, a, cus, &rtiles, &chunks);
+  *bytes_out = workspace_layout(pool, a, single ? 0 : num_waves_for(a, cus), single, chunks).total;
   return PKV_OK;
 }
 
@@ -1360,33 +1618,58 @@ static pkv_status decode_launch(const kv_pool* pool, const paged_decode_args* a,
   P.ws_o = nullptr;
   P.ws_ml = nullptr;
   P.ws_job = nullptr;
+  P.ws_pre = nullptr;
   P.xcd_remap = 0;
+  P.shared = a->shared_prefix_blocks;
+  P.pre_chunks = 0;
+  P.pre_rtiles = 0;
   decode_fn fn = pick_decode(d.kv_dtype, d.head_dim, d.block_size);
   if (!fn) return fail(PKV_E_UNSUPPORTED, "no kernel for this shape");
   hipStream_t s = (hipStream_t)stream;
   const int64_t segs = (int64_t)d.num_kv_heads * a->batch;
+  // a shared prefix always runs in range mode (its merge joins the prefix)
+  const bool single = P.shared == 0 && (a->num_splits == 1 || a->max_blocks_per_seq == 0);
 
-  if (a->num_splits == 1 || a->max_blocks_per_seq == 0) {
+  int cus = 0;
+  if ((!single && a->num_splits <= 1) || P.shared > 0) {
+    st = device_cus(&cus);
+    if (st != PKV_OK) return st;
+  }
+  const int64_t W = single ? 0 : num_waves_for(a, cus);
+  if (P.shared > 0) prefix_plan(pool, a, cus, &P.pre_rtiles, &P.pre_chunks);
+  const WsLayout wl = workspace_layout(pool, a, W, single, P.pre_chunks);
+  char* ws = reinterpret_cast<char*>(a->workspace);
+  if (wl.total > 0) {
+    if (!a->workspace || a->workspace_bytes < wl.total)
+      return fail(PKV_E_INVAL, "workspace missing or smaller than paged_attention_workspace_size()");
+    if (reinterpret_cast<uintptr_t>(a->workspace) % 256)
+      return fail(PKV_E_INVAL, "workspace must be 256-byte aligned");
+  }
+  // the first kernel launched records ev[0]
+  hipEvent_t ev_first = ev ? ev[0] : nullptr;
+  hipError_t e;
+  if (P.shared > 0) {
+    P.ws_pre = reinterpret_cast<float*>(ws + wl.pre_off);
+    decode_fn pfn = pick_prefix(d.kv_dtype, d.head_dim, d.block_size);
+    if (!pfn) return fail(PKV_E_UNSUPPORTED, "no kernel for this shape");
+    const int64_t tasks = (int64_t)d.num_kv_heads * P.pre_rtiles * P.pre_chunks;
+    int64_t pgrid = (tasks + 3) / 4;
+    pgrid = ((pgrid + 7) / 8) * 8;  // whole rounds over the 8 XCDs
+    e = launch(pfn, dim3((uint32_t)pgrid), 0, s, ev_first, nullptr, P);
+    if (e != hipSuccess) return hip_fail(e, "prefix launch");
+    ev_first = nullptr;
+  }
+
+  if (single) {
     P.single = 1;
     P.num_waves = 0;
     const int64_t grid = (segs + 3) / 4;
-    hipError_t e = launch(fn, dim3((uint32_t)grid), 0, s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, P);
+    e = launch(fn, dim3((uint32_t)grid), 0, s, ev_first, ev ? ev[1] : nullptr, P);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     if (nk) *nk = 1;
     return PKV_OK;
   }
 
-  int cus = 0;
-  if (a->num_splits == 0) {
-    st = device_cus(&cus);
-    if (st != PKV_OK) return st;
-  }
-  const int64_t W = num_waves_for(a, cus);
-  const WsLayout wl = workspace_layout(pool, a, W);
-  if (!a->workspace || a->workspace_bytes < wl.total)
-    return fail(PKV_E_INVAL, "workspace missing or smaller than paged_attention_workspace_size()");
-  if (reinterpret_cast<uintptr_t>(a->workspace) % 256) return fail(PKV_E_INVAL, "workspace must be 256-byte aligned");
-  char* ws = reinterpret_cast<char*>(a->workspace);
   P.ws_o = reinterpret_cast<float*>(ws + wl.o_off);
   P.ws_ml = reinterpret_cast<float*>(ws + wl.ml_off);
   P.ws_job = reinterpret_cast<int4*>(ws + wl.job_off);
@@ -1396,7 +1679,7 @@ static pkv_status decode_launch(const kv_pool* pool, const paged_decode_args* a,
   grid = ((grid + 7) / 8) * 8;  // whole rounds over the 8 XCDs
   P.xcd_remap = 1;
   const size_t lds = (size_t)(a->batch + 1) * sizeof(int32_t);
-  hipError_t e = launch(fn, dim3((uint32_t)grid), lds, s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, P);
+  e = launch(fn, dim3((uint32_t)grid), lds, s, ev_first, ev ? ev[1] : nullptr, P);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   if (nk) *nk = 1;
   // few sequence-heads: spread each one's output positions over several

@@ -397,6 +397,33 @@ pkv_status block_table_get(const kv_pool* p, int32_t seq, int32_t* blocks_out, i
   return PKV_OK;
 }
 
+pkv_status block_table_common_prefix(const kv_pool* p, const int32_t* seqs, int32_t n, int32_t* blocks_out) {
+  if (!p || !blocks_out || n < 0 || (n > 0 && !seqs)) return fail(PKV_E_INVAL, "bad argument");
+  PKV_GUARD_BEGIN
+  p->batch.resize(n);
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = const_cast<kv_pool*>(p)->seqs.find(seqs[i]);
+    if (it == p->seqs.end()) return fail(PKV_E_INVAL, "unknown sequence id");
+    p->batch[i] = &it->second;
+  }
+  int64_t k = 0;
+  if (n > 0) {
+    const Sequence& s0 = *p->batch[0];
+    k = (int64_t)s0.table.size();
+    for (int32_t i = 0; i < n; ++i) {
+      const Sequence& s = *p->batch[i];
+      k = std::min<int64_t>(k, s.len / p->desc.block_size);   // full blocks only
+      k = std::min<int64_t>(k, (int64_t)s.table.size());
+      int64_t j = 0;
+      while (j < k && s.table[j] == s0.table[j] && s0.table[j] >= 0) ++j;
+      k = j;
+    }
+  }
+  *blocks_out = (int32_t)k;
+  return PKV_OK;
+  PKV_GUARD_END
+}
+
 pkv_status block_table_export(const kv_pool* p, const int32_t* seqs, int32_t n,
                               int32_t max_blocks, int32_t* tables_out, int32_t* lens_out) {
   if (!p || n < 0 || max_blocks < 0 ||

@@ -124,6 +124,10 @@ def test_block_manager_matches_oracle(seed):
                     c_slots, c_cows = P.block_table_append(h, s, n)
                     assert c_slots.tolist() == o_slots and c_cows == o_cows
             _same_state(h, bm, ids)
+            now = list(ids)
+            if now and rng.random() < 0.3:
+                batch = rng.sample(now, rng.randint(1, len(now)))
+                assert P.block_table_common_prefix(h, batch) == bm.common_prefix([ids[s] for s in batch])
         if ids:
             seqs = list(ids)
             mb = max(len(bm.table(ids[s])) for s in seqs) + 1
@@ -298,3 +302,34 @@ def test_metadata_upload_rejects_bad_arguments_on_host():
     with pytest.raises(P.PagedKVError):
         P.kv_metadata_upload(4096, 8192, 18, 0)
     P.kv_metadata_upload(4096, 8192, 0, 0)   # nothing to copy: no-op
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_common_prefix_of_fork_trees_matches_oracle(seed):
+    # random fork trees with appends (copy-on-write of shared partial blocks):
+    # the shared leading blocks of random subsets agree with the oracle
+    rng = random.Random(100 + seed)
+    nb, bs = 400, rng.choice([4, 16])
+    h, bm = _pair(nb, bs, None)
+    try:
+        root_c, root_o = P.block_table_alloc(h), bm.alloc()
+        n = rng.randint(0, 6 * bs)
+        P.block_table_append(h, root_c, n)
+        bm.append(root_o, n)
+        ids = {root_c: root_o}
+        for _ in range(40):
+            p = rng.choice(list(ids))
+            c, o = P.block_table_fork(h, p), bm.fork(ids[p])
+            ids[c] = o
+            n = rng.randint(0, 2 * bs)
+            P.block_table_append(h, c, n)
+            bm.append(o, n)
+        live = list(ids)
+        for _ in range(30):
+            batch = rng.sample(live, rng.randint(1, len(live)))
+            assert P.block_table_common_prefix(h, batch) == bm.common_prefix([ids[s] for s in batch])
+        assert P.block_table_common_prefix(h, []) == 0
+        with pytest.raises(P.PagedKVError):
+            P.block_table_common_prefix(h, [10 ** 6])
+    finally:
+        P.kv_pool_destroy(h)

@@ -96,7 +96,7 @@ class FullState:
         if to_oracle:
             self.opool.append(0, kb, vb, self.w.src_dtype, oslots)
 
-    def decode(self, seqs, oseqs, q):
+    def decode(self, seqs, oseqs, q, shared=0, splits=0):
         w = self.w
         mb = max(len(self.bm.table(o)) for o in oseqs)
         tables, lens = P.block_table_export(self.pool.handle, seqs, mb)
@@ -106,7 +106,7 @@ class FullState:
         out = torch.full((B, w.num_q_heads, w.head_dim), float("nan"), dtype=torch.float32, device="cuda")
         qd, td, ld = to_dev(q), torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda()
         a = P.make_decode_args(0, B, w.num_q_heads, mb, qd, w.q_dtype, td, ld, 1.0 / math.sqrt(w.head_dim), out,
-                               "f32", sliding_window=w.window, num_splits=0)
+                               "f32", sliding_window=w.window, num_splits=splits, shared_prefix_blocks=shared)
         nbytes = P.paged_attention_workspace_size(self.pool.handle, a)
         ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
         a.workspace, a.workspace_bytes = ws.data_ptr(), nbytes
@@ -173,6 +173,12 @@ def test_full_size_prefix_shared_step():
         st.opool.append(0, kb, vb, w.src_dtype, oslots)
         got, ot, ol = st.decode(branches, obranches, qb)
         st.check(got, qb, ot, ol, sample)
+        # the same step reading the shared prefix once (f1)
+        k = P.block_table_common_prefix(h, branches)
+        assert k == st.bm.common_prefix(obranches) == w.prefix_len // w.block_size
+        got_s, _, _ = st.decode(branches, obranches, qb, shared=k)
+        st.check(got_s, qb, ot, ol, sample)
+        assert np.abs(got_s - got).max() <= 2 * TOL[w.kv_dtype]
         P.block_table_free_batch(h, branches)
         for o in obranches:
             st.bm.free(o)

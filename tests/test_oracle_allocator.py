@@ -301,3 +301,50 @@ def test_window_release_bounds_held_blocks():
     assert slots[0] == bm.table(s)[1000 // bs] * bs + 1000 % bs
     with pytest.raises(AllocatorError):
         bm.release_before(s, 1002)
+
+
+def test_common_prefix_of_fork_families():
+    # pages: a shared prefix is stored once and reference counted; forked
+    # sequences hold the parent's blocks until they write into them.  The
+    # common prefix is the run of leading blocks that are the same physical
+    # blocks in every sequence and full in all of them.
+    bs = 16
+    bm = BlockManager(64, bs)
+    root = bm.alloc()
+    bm.append(root, 100)                       # 6 full blocks + 4 tokens in block 6
+    kids = [bm.fork(root) for _ in range(5)]
+    assert bm.common_prefix(kids) == 100 // bs == 6       # block 6 is shared but not full
+    assert bm.common_prefix([root] + kids) == 6
+    for k, n in zip(kids, (1, 2, 3, 1, 40)):
+        _, cows = bm.append(k, n)
+        assert len(cows) == 1                  # each copies the shared partial block 6
+    assert bm.common_prefix(kids) == 6
+    assert bm.common_prefix([kids[4]]) == (100 + 40) // bs  # one sequence: its full blocks
+    # exact multiple: children take fresh blocks, the 6 full ones stay shared
+    r2 = bm.alloc()
+    bm.append(r2, 96)
+    a, b = bm.fork(r2), bm.fork(r2)
+    bm.append(a, 17)
+    bm.append(b, 1)
+    assert bm.common_prefix([a, b]) == 6
+    # nested forks share more with each other than with the root
+    c1, c2 = bm.fork(a), bm.fork(a)
+    bm.append(c1, 5)
+    bm.append(c2, 5)
+    assert bm.common_prefix([c1, c2]) == (96 + 17) // bs == 7
+    assert bm.common_prefix([r2, c1]) == 6
+    # unrelated sequences share nothing; an empty batch has no prefix
+    assert bm.common_prefix([root, r2]) == 0
+    assert bm.common_prefix([]) == 0
+
+
+def test_common_prefix_stops_at_released_blocks():
+    bm = BlockManager(32, 16)
+    root = bm.alloc()
+    bm.append(root, 80)
+    kids = [bm.fork(root) for _ in range(3)]
+    assert bm.common_prefix(kids) == 5
+    bm.release_before(kids[0], 40)             # kids[0] drops blocks 0 and 1 (entries -1)
+    assert bm.common_prefix(kids) == 0
+    assert bm.common_prefix(kids[1:]) == 5
+    assert bm.common_prefix([kids[0]]) == 0
