@@ -222,9 +222,13 @@ def run(args):
     sptr = stream.cuda_stream
     out = torch.empty((B, w.num_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
     scale = 1.0 / math.sqrt(w.head_dim)
+    # shared-prefix decode for forked families: the prefix's full blocks
+    shared0 = 0
+    if w.lengths_kind == "prefix" and not args.no_shared_prefix:
+        shared0 = w.prefix_len // w.block_size
     args0 = P.make_decode_args(0, B, w.num_q_heads, reps[0].max_blocks, steps[0][2], w.q_dtype,
                                reps[0].d_tables, reps[0].d_lens, scale, out, "f32",
-                               sliding_window=w.window, num_splits=args.splits)
+                               sliding_window=w.window, num_splits=args.splits, shared_prefix_blocks=shared0)
     ws_bytes = P.paged_attention_workspace_size(reps[0].pool.handle, args0)
     ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
     # pinned staging ring for the per-step metadata; a buffer is rewritten only
@@ -255,7 +259,8 @@ def run(args):
         rep = reps[t % len(reps)]
         dec_args.append(P.make_decode_args(0, B, w.num_q_heads, mb, steps[t][2], w.q_dtype, rep.d_tables,
                                            rep.d_lens, scale, out, "f32", sliding_window=w.window,
-                                           num_splits=args.splits, workspace=ws, workspace_bytes=ws_bytes))
+                                           num_splits=args.splits, workspace=ws, workspace_bytes=ws_bytes,
+                                           shared_prefix_blocks=shared0))
     # Every TIME_EVERY-th step's decode is timed by its own kernels (attention
     # start/end, merge start/end).  Recording an event ends a kernel with a
     # system-scope release (a few idle microseconds), so only a sample of
@@ -294,6 +299,12 @@ def run(args):
             rep.lengths += 1
         _, cows = P.block_table_append_batch(h, seqs, slots_out=slots_np, cow_out=cows_np)
         P.block_table_export(h, seqs, mb, tables_out=tables_np, lens_out=lens_np)
+        if shared0:
+            # the blocks the batch holds in common, read once by the decode
+            k = P.block_table_common_prefix(h, seqs)
+            if k != shared0:
+                raise RuntimeError(f"common prefix {k} blocks, expected {shared0}")
+            dec_args[t].shared_prefix_blocks = k
         P.kv_metadata_upload(rep.meta, buf, meta_bytes, sptr)
         if len(cows):
             P.kv_pool_copy_blocks(h, rep.d_cows, len(cows), sptr)
@@ -387,7 +398,7 @@ def run(args):
             "batch": B, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
             "head_dim": w.head_dim, "block_size": w.block_size, "kv_dtype": w.kv_dtype,
             "mean_context": float(np.mean(d.lengths)), "sliding_window": w.window,
-            "num_splits": args.splits, "replicas": len(reps),
+            "num_splits": args.splits, "replicas": len(reps), "shared_prefix_blocks": shared0,
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "seq_heads_per_s": round(B * w.num_q_heads / (step_ms * 1e-3), 1),
@@ -401,7 +412,8 @@ def run(args):
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "paged_attention_decode (decode_kernel + merge_kernel)",
+            "kernel": "paged_attention_decode (" + ("prefix_kernel + " if shared0 else "")
+                      + "decode_kernel + merge_kernel)",
         },
         "decode_timing": f"sum of the call's kernel durations, recorded by the kernels themselves "
                          f"(hipExtLaunchKernelGGL events) on {len(dec_ms)} of the {args.steps} timed steps",
@@ -523,6 +535,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-shared-prefix", action="store_true",
+                    help="decode forked families without reading their common prefix once")
     ap.add_argument("--traffic", type=float, default=None,
                     help="HBM bytes per decode call from rocprofv3 counters (GB)")
     ap.add_argument("--copy-probe", type=int, default=0,

@@ -237,7 +237,7 @@ struct DecodeParams {
   // sequence, query head) in ws_pre, and merge_kernel folds them in
   int32_t shared;     // 0: off
   int32_t pre_chunks; // token chunks of the prefix
-  int32_t pre_rtiles; // query-row tiles per KV head
+  int32_t pre_rtiles; // query-row groups (one workgroup each) per KV head
   float* ws_pre;      // [pre_chunks + 1][B * Hq][D + 4]: o, max, sum, 2 pad
 };
 
@@ -350,6 +350,25 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 load_stream(const uint8_t* p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// 16 bytes per lane from global memory straight into LDS (gfx950
+// global_load_lds_dwordx4): lane l's bytes land at LDS byte address
+// lds_wave_base + 16 * l.  Written as inline assembly so that the compiler
+// does not wait for these loads before every LDS read; the caller waits with
+// wait_vmem and a barrier.  M0 (the LDS base) is set inside the same
+// statement, right before the load.
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds_wave_base), "v"(src) : "memory");
+}
+
+// Wait until at most N vector-memory loads of this wavefront are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+  // gfx9 s_waitcnt: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14;
+  // expcnt (bits 6:4) and lgkmcnt (bits 11:8) left at their maxima
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 // 16 bytes as 8 x 16-bit MFMA operand elements
@@ -545,20 +564,43 @@ struct Decoder {
     }
   }
 
+  // Every lane's tokens of the sub-tile lie in a real block and in [lo, L),
+  // so nothing needs masking (the same answer in every lane).
+  static __device__ __forceinline__ bool tile_full(const VTile& T, int32_t lo, int32_t L, int kg) {
+    const int32_t t0 = T.tok0 + TPG * kg;
+    return __all(T.ok && t0 >= lo && t0 + TPG <= L);
+  }
+
+  // The exponentials of a (head, piece) are taken relative to a reference
+  // maximum st.m that moves only when a score exceeds it by more than 2^8:
+  // o and l are then at most 2^8 times larger than with the running maximum,
+  // far from fp32 limits, and o / l -- like every use of (o, m, l) -- does not
+  // depend on which reference was used.  So O is rescaled a few times per
+  // piece instead of at every sub-tile.
+  static constexpr float RESCALE_LOG2 = 8.0f;
+
   // Online softmax over one scored sub-tile: probabilities p of this lane's
-  // tokens (0 where not attended), running max / sum, O rescaled.
+  // tokens (0 where not attended), reference maximum, sum, O rescaled when
+  // the reference moves.
   static __device__ __forceinline__ void softmax(const VTile& T, const f32x4 (&S)[NQT], State& st,
                                                  float (&p)[NQT][4], int32_t lo, int32_t L, float scale_log2,
                                                  int kg) {
     float s[NQT][4];
+    if (tile_full(T, lo, L, kg)) {
 #pragma unroll
-    for (int t = 0; t < NQT; ++t)
+      for (int t = 0; t < NQT; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int32_t tok = T.tok0 + TPG * kg + 4 * t + r;
-        const bool valid = T.ok && tok >= lo && tok < L;
-        s[t][r] = valid ? S[t][r] * scale_log2 : -INFINITY;
-      }
+        for (int r = 0; r < 4; ++r) s[t][r] = S[t][r] * scale_log2;
+    } else {
+#pragma unroll
+      for (int t = 0; t < NQT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int32_t tok = T.tok0 + TPG * kg + 4 * t + r;
+          const bool valid = T.ok && tok >= lo && tok < L;
+          s[t][r] = valid ? S[t][r] * scale_log2 : -INFINITY;
+        }
+    }
     float bmax = s[0][0];
 #pragma unroll
     for (int t = 0; t < NQT; ++t)
@@ -566,9 +608,15 @@ struct Decoder {
       for (int r = 0; r < 4; ++r) bmax = fmaxf(bmax, s[t][r]);
     bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
     bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-    const float m_new = fmaxf(st.m, bmax);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(st.m - m_use);
+    const bool up = bmax > st.m + RESCALE_LOG2;   // the first finite score always moves it
+    if (__any(up)) {
+      const float alpha = up ? __builtin_amdgcn_exp2f(st.m - bmax) : 1.0f;
+      st.m = up ? bmax : st.m;
+      st.l *= alpha;
+#pragma unroll
+      for (int n = 0; n < NV; ++n) st.O[n] *= alpha;
+    }
+    const float m_use = st.m == -INFINITY ? 0.f : st.m;
     float psum = 0.f;
 #pragma unroll
     for (int t = 0; t < NQT; ++t)
@@ -577,30 +625,29 @@ struct Decoder {
         p[t][r] = __builtin_amdgcn_exp2f(s[t][r] - m_use);
         psum += p[t][r];
       }
-    st.l = st.l * alpha + psum;
-    st.m = m_new;
-#pragma unroll
-    for (int n = 0; n < NV; ++n) st.O[n] *= alpha;
+    st.l += psum;
   }
 
   // O += P.V over one sub-tile.  Tokens that are not attended may hold any
   // bits (NaN): their V elements are zeroed first (bit masks, no branch).
   static __device__ __forceinline__ void pv(VTile& T, const float (&p)[NQT][4], State& st, int32_t lo, int32_t L,
                                             int kg) {
-    uint32_t vmask[4] = {0u, 0u, 0u, 0u};
+    if (!tile_full(T, lo, L, kg)) {
+      uint32_t vmask[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int e = 0; e < TPG; ++e) {
-      const int32_t tok = T.tok0 + TPG * kg + e;
-      const bool valid = T.ok && tok >= lo && tok < L;
-      const uint32_t field = EB == 4 ? 0xffffffffu : (EB == 2 ? 0xffffu : 0xffu);
-      vmask[e / EPW] |= valid ? field << (8 * EB * (e % EPW)) : 0u;
-    }
+      for (int e = 0; e < TPG; ++e) {
+        const int32_t tok = T.tok0 + TPG * kg + e;
+        const bool valid = T.ok && tok >= lo && tok < L;
+        const uint32_t field = EB == 4 ? 0xffffffffu : (EB == 2 ? 0xffffu : 0xffu);
+        vmask[e / EPW] |= valid ? field << (8 * EB * (e % EPW)) : 0u;
+      }
 #pragma unroll
-    for (int n = 0; n < NV; ++n) {
-      T.v[n].x &= vmask[0];
-      T.v[n].y &= vmask[1];
-      T.v[n].z &= vmask[2];
-      T.v[n].w &= vmask[3];
+      for (int n = 0; n < NV; ++n) {
+        T.v[n].x &= vmask[0];
+        T.v[n].y &= vmask[1];
+        T.v[n].z &= vmask[2];
+        T.v[n].w &= vmask[3];
+      }
     }
     if constexpr (KV == KV_F32) {
 #pragma unroll
@@ -795,16 +842,28 @@ struct Decoder {
 
   // Query-row tiles (MFMA column blocks of 16 rows) per wavefront of prefix_kernel.
   static constexpr int NT = 2;
+  // 16-byte K and V groups of one sub-tile: one per lane per load of load_k /
+  // load_v, so a wavefront's loads of a sub-tile are exactly the sub-tile.
+  static constexpr int KG = NKL * 64;
+  static constexpr int VG = NV * 64;
+  // LDS bytes of one staged sub-tile (three are used)
+  static constexpr int STAGE_BYTES = (KG + VG) * 16;
+  static constexpr int STAGES = 3;
 
-  // Shared prefix, one wavefront: query rows rt*16*NT .. +16*NT of KV head g
-  // (row r = sequence r / G, head g*G + r % G) against token chunk c of the
-  // prefix (row 0's first `shared` blocks), every K/V sub-tile used for all of
-  // its rows.  Each row attends prefix tokens below min(its L, prefix).
-  // Writes the chunk's partial (o in output units, max, sum) of every row.
-  static __device__ void prefix_piece(const DecodeParams& P, int g, int rt, int c) {
-    const int lane = threadIdx.x & 63;
+  // Shared prefix, one workgroup of 4 wavefronts: query rows
+  // rg*64*NT .. +64*NT of KV head g (wavefront wv takes 16*NT of them; row
+  // r = sequence r / G, head g*G + r % G) against token chunk c of the prefix
+  // (row 0's first `shared` blocks).  Every K/V sub-tile is fetched from
+  // global memory once per workgroup, staged in LDS in the order in which a
+  // wavefront's lanes use it, and read from there by all four wavefronts.
+  // Each row attends the prefix tokens below min(its L, prefix).  Writes the
+  // chunk's partial (o in output units, max, sum) of every row.
+  static __device__ void prefix_group(const DecodeParams& P, int g, int rg, int c, uint8_t* lds) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
     const int i = lane & 15;
     const int kg = lane >> 4;
+    const int wv = uniform(tid >> 6);
     const int G = P.group;
     const int64_t nrows = (int64_t)P.batch * G;
     const int32_t kT = P.shared * BS;
@@ -816,7 +875,7 @@ struct Decoder {
     bool live[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const int64_t r = (int64_t)rt * 16 * NT + t * 16 + i;
+      const int64_t r = ((int64_t)rg * 4 + wv) * 16 * NT + t * 16 + i;
       live[t] = r < nrows;
       const int b = live[t] ? (int)(r / G) : 0;
       const int hg = live[t] ? (int)(r % G) : 0;
@@ -834,69 +893,87 @@ struct Decoder {
     const int32_t s0 = (int32_t)((int64_t)c * nsp / P.pre_chunks);
     const int32_t s1 = (int32_t)((int64_t)(c + 1) * nsp / P.pre_chunks);
 
-    // row 0's table entries of the prefix, 64 at a time, one per lane
-    int ccur = -1;
-    int32_t tcur = -1;
-    auto where = [&](int32_t s) -> Addr {
+    // row 0's table entries of the prefix, 64 at a time, one per lane; one
+    // cache for the loads and one for the math, which run two sub-tiles apart
+    struct TabCache {
+      int cc = -1;
+      int32_t t = -1;
+    } tab_load, tab_math;
+    // the addresses this lane would load sub-tile s from
+    auto where = [&](int32_t s, TabCache& tc) -> Addr {
       const int32_t tok = s * TT;
       const int32_t rel = (tok / U) * UB;  // first table entry of the unit
       const int cc = rel >> 6;
-      if (cc != ccur) {
-        tcur = table_chunk(P, 0, 0, P.shared, cc, lane);
-        ccur = cc;
+      if (cc != tc.cc) {
+        tc.t = table_chunk(P, 0, 0, P.shared, cc, lane);
+        tc.cc = cc;
       }
       int32_t ids[UB];
 #pragma unroll
-      for (int k = 0; k < UB; ++k) ids[k] = __builtin_amdgcn_readlane(tcur, (rel & 63) + k);
+      for (int k = 0; k < UB; ++k) ids[k] = __builtin_amdgcn_readlane(tc.t, (rel & 63) + k);
       return locate(P, g, ids, (tok % U) / TT, tok, i, kg);
+    };
+    // Stage sub-tile s in LDS slot `slot` with global-to-LDS loads: the
+    // workgroup's 256 threads move its KG + VG 16-byte groups, group
+    // x = 256u + 64 * wave + lane being load x / 64 of lane x % 64 (K loads
+    // first, then V), so that a wavefront later reads group m * 64 + lane as
+    // its m-th load.  Each load writes 16 bytes per lane at the wavefront's
+    // LDS base + 16 * lane.
+    constexpr int NG = (KG + VG) / 256;
+    const uint32_t lds0 = uniform((uint32_t)(uintptr_t)lds);
+    auto issue = [&](int32_t s, int slot) {
+      const Addr a = where(s, tab_load);
+#pragma unroll
+      for (int u = 0; u < NG; ++u) {
+        const int x0 = 256 * u + 64 * wv;  // uniform
+        const uint8_t* src;
+        if (x0 < KG) {
+          const int m = x0 >> 6;            // QK tile m / NKJ, step m % NKJ
+          src = a.krow + (4 * (m % NKJ) * BS + 4 * (m / NKJ)) * 16;
+        } else {
+          src = a.vrow + 16 * ((x0 - KG) >> 6) * BS * EB;
+        }
+        lds_dma16(src, lds0 + (uint32_t)(slot * STAGE_BYTES + x0 * 16));
+      }
     };
 
     if (s0 < s1) {
-      KTile K0, K1;
-      VTile V0, V1;
+      // three LDS slots: two sub-tiles in flight while one is used
+      issue(s0, 0);
+      if (s0 + 1 < s1) issue(s0 + 1, 1);
+      KTile K;
+      VTile V;
       f32x4 S[NQT];
       float pp[NT][NQT][4];
-      Addr a0 = where(s0), a1;
-      load_k(K0, a0);
-      load_v(V0, a0);
-      // the staggered two-buffer pipeline of stream(), each sub-tile scored
-      // and accumulated for all NT row tiles
-      for (int32_t s = s0; s < s1; s += 2) {
-        const bool n1 = s + 1 < s1;
-        if (n1) {
-          a1 = where(s + 1);
-          load_k(K1, a1);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+      int slot = 0;
+      for (int32_t s = s0; s < s1; ++s) {
+        // slot (s + 2) % 3 was last read in iteration s - 1, before its
+        // closing barrier
+        const int ahead = (s + 2 < s1) ? 2 : (s + 1 < s1 ? 1 : 0);
+        if (ahead == 2) issue(s + 2, slot == 0 ? 2 : slot - 1);
+        // sub-tile s has landed once no more than `ahead` stages (NG loads
+        // each) are outstanding: this thread's, then every thread's
+        if (ahead == 2) wait_vmem<2 * NG>();
+        else if (ahead == 1) wait_vmem<NG>();
+        else wait_vmem<0>();
+        __syncthreads();
+        const uint4* src = reinterpret_cast<const uint4*>(lds + slot * STAGE_BYTES);
+#pragma unroll
+        for (int m = 0; m < NKL; ++m) K.k[m] = src[m * 64 + lane];
+#pragma unroll
+        for (int n = 0; n < NV; ++n) V.v[n] = src[KG + n * 64 + lane];
+        const Addr a = where(s, tab_math);
+        V.tok0 = a.tok0;
+        V.ok = a.ok;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          qk(K0, q[t], S);
-          softmax(V0, S, st[t], pp[t], 0, Lc[t], P.scale_log2, kg);
+          qk(K, q[t], S);
+          softmax(V, S, st[t], pp[t], 0, Lc[t], P.scale_log2, kg);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        if (n1) load_v(V1, a1);
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int t = 0; t < NT; ++t) pv(V0, pp[t], st[t], 0, kT, kg);
-        __builtin_amdgcn_sched_barrier(0);
-        if (!n1) break;
-        const bool n2 = s + 2 < s1;
-        if (n2) {
-          a0 = where(s + 2);
-          load_k(K0, a0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          qk(K1, q[t], S);
-          softmax(V1, S, st[t], pp[t], 0, Lc[t], P.scale_log2, kg);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        if (n2) load_v(V0, a0);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) pv(V1, pp[t], st[t], 0, kT, kg);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int t = 0; t < NT; ++t) pv(V, pp[t], st[t], 0, kT, kg);
+        __syncthreads();   // every wavefront is done with this slot
+        slot = slot == 2 ? 0 : slot + 1;
       }
     }
 
@@ -1128,21 +1205,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 }
 
-// Shared prefix: wavefront w takes (KV head g, query-row tile rt, token
-// chunk c), KV-head major, so the ranges of one head sit on one XCD and its
-// prefix blocks stay in that XCD's L2.
+// Shared prefix: workgroup x takes (KV head g, row group rg, token chunk c),
+// KV-head major, so the workgroups of one head sit on one XCD and its prefix
+// blocks stay in that XCD's L2.
 template <int KV, int D, int BS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefix_kernel(DecodeParams P) {
   typedef Decoder<KV, D, BS> Dec;
-  const int wid = uniform((int)(threadIdx.x >> 6));
+  __shared__ __attribute__((aligned(16))) uint8_t stage[Dec::STAGES * Dec::STAGE_BYTES];
   int64_t wg = blockIdx.x;
   wg = (wg % 8) * (gridDim.x / 8) + wg / 8;
-  const int64_t w = wg * 4 + wid;
   const int64_t per_head = (int64_t)P.pre_rtiles * P.pre_chunks;
-  if (w >= per_head * P.hkv) return;
-  const int g = uniform((int)(w / per_head));
-  const int64_t rem = w % per_head;
-  Dec::prefix_piece(P, g, uniform((int)(rem / P.pre_chunks)), uniform((int)(rem % P.pre_chunks)));
+  if (wg >= per_head * P.hkv) return;   // whole workgroup: no barrier is skipped
+  const int g = (int)(wg / per_head);
+  const int64_t rem = wg % per_head;
+  Dec::prefix_group(P, g, (int)(rem / P.pre_chunks), (int)(rem % P.pre_chunks), stage);
 }
 
 // Log-sum-exp merge of the pieces of a split (KV head, sequence).  Workgroup
@@ -1344,17 +1420,18 @@ static int tokens_per_subtile(int kv) {
   return kv == PKV_F32 ? SubTile<KV_F32>::TT : (kv == PKV_FP8_E4M3 ? SubTile<KV_FP8>::TT : SubTile<KV_BF16>::TT);
 }
 
-// Shared prefix work split: query-row tiles per KV head and token chunks,
-// about two wavefronts per CU in all, at most 16 chunks.
+// Shared prefix work split: row groups (128 query rows, one workgroup) per
+// KV head and token chunks, about one workgroup per CU in all, at most 16
+// chunks.
 static void prefix_plan(const kv_pool* pool, const paged_decode_args* a, int cus, int32_t* rtiles,
                         int32_t* chunks) {
   const kv_pool_desc& d = pool->desc;
-  constexpr int rows_per_wave = 16 * Decoder<KV_BF16, 128, 16>::NT;
+  constexpr int rows_per_group = 4 * 16 * Decoder<KV_BF16, 128, 16>::NT;
   const int64_t G = a->num_q_heads / d.num_kv_heads;
-  const int64_t rt = ((int64_t)a->batch * G + rows_per_wave - 1) / rows_per_wave;
+  const int64_t rt = ((int64_t)a->batch * G + rows_per_group - 1) / rows_per_group;
   const int64_t tt = tokens_per_subtile(d.kv_dtype);
   const int64_t nsp = ((int64_t)a->shared_prefix_blocks * d.block_size + tt - 1) / tt;
-  int64_t c = (2 * (int64_t)cus) / std::max<int64_t>(1, d.num_kv_heads * rt);
+  int64_t c = (int64_t)cus / std::max<int64_t>(1, d.num_kv_heads * rt);
   c = std::max<int64_t>(1, std::min<int64_t>({c, nsp, 16}));
   *rtiles = (int32_t)rt;
   *chunks = (int32_t)c;
@@ -1653,8 +1730,7 @@ static pkv_status decode_launch(const kv_pool* pool, const paged_decode_args* a,
     decode_fn pfn = pick_prefix(d.kv_dtype, d.head_dim, d.block_size);
     if (!pfn) return fail(PKV_E_UNSUPPORTED, "no kernel for this shape");
     const int64_t tasks = (int64_t)d.num_kv_heads * P.pre_rtiles * P.pre_chunks;
-    int64_t pgrid = (tasks + 3) / 4;
-    pgrid = ((pgrid + 7) / 8) * 8;  // whole rounds over the 8 XCDs
+    const int64_t pgrid = ((tasks + 7) / 8) * 8;  // one workgroup per task, whole rounds over the 8 XCDs
     e = launch(pfn, dim3((uint32_t)pgrid), 0, s, ev_first, nullptr, P);
     if (e != hipSuccess) return hip_fail(e, "prefix launch");
     ev_first = nullptr;
