@@ -206,6 +206,46 @@ pkv_status block_table_common_prefix(const kv_pool* pool, const int32_t* seqs, i
 pkv_status block_table_export(const kv_pool* pool, const int32_t* seqs, int32_t n,
                               int32_t max_blocks, int32_t* tables_out, int32_t* lens_out);
 
+/* ---- prefix cache (host only; page "第2章 KV Cache：模型内部的显存复用",
+ *      chapter summary and section 2.4: a radix tree organises the prefixes
+ *      of multi-turn conversations into a cache that later requests hit;
+ *      page "生成一个字…", section "PagedAttention：…": shared blocks are
+ *      stored once, reference counted) ----
+ * A radix tree over token ids whose edges hold runs of whole blocks of one
+ * pool.  Granularity is the block: only full blocks are cached or matched.
+ * The cache holds one reference on each block it caches (so the blocks stay
+ * allocated after the sequences that wrote them are freed) and never caches
+ * the same tokens under the same prefix twice.  Every match or insert
+ * touches the blocks on its path (one clock tick per call); eviction gives
+ * back, one block at a time, the deepest block of the least recently touched
+ * leaf whose block no sequence holds.  The pool must outlive the cache.  Not
+ * thread-safe: calls on a pool and its cache are serialised by the caller. */
+typedef struct kv_prefix_cache kv_prefix_cache;
+
+pkv_status prefix_cache_create(kv_pool* pool, kv_prefix_cache** out);
+/* Drops every reference the cache holds (in eviction order) and frees it. */
+void prefix_cache_destroy(kv_prefix_cache* cache);
+/* Longest cached prefix of tokens[0 .. n) in whole blocks.  Always creates a
+ * new sequence (*seq_out) holding the matched blocks (one more reference
+ * each, as a fork would) with length *matched_out = the matched tokens, a
+ * multiple of block_size (0 on a miss).  The caller appends the rest of the
+ * prompt to it.  PKV_E_INVAL for bad arguments; on failure nothing changes. */
+pkv_status prefix_cache_match(kv_prefix_cache* cache, const int32_t* tokens, int32_t n,
+                              int32_t* seq_out, int32_t* matched_out);
+/* Caches the full blocks of seq that tokens[0 .. n) describe (the first
+ * min(n, length) / block_size blocks, up to the first released entry).  Blocks
+ * whose tokens are already cached under the same prefix are not added; the
+ * rest get one reference from the cache.  tokens must be the tokens whose K/V
+ * the sequence holds.  PKV_E_INVAL for an unknown id. */
+pkv_status prefix_cache_insert(kv_prefix_cache* cache, int32_t seq, const int32_t* tokens, int32_t n);
+/* Gives back up to n_blocks cached blocks that no sequence holds, least
+ * recently used leaves first, deepest block first; *freed_out: how many went
+ * back to the free queue (fewer when nothing else can be evicted). */
+pkv_status prefix_cache_evict(kv_prefix_cache* cache, int32_t n_blocks, int32_t* freed_out);
+/* Blocks the cache holds and tree nodes (edges). */
+pkv_status prefix_cache_stats(const kv_prefix_cache* cache, int32_t* cached_blocks_out,
+                              int32_t* nodes_out);
+
 /* ---- device work ---- */
 
 /* Whole-block copies for copy-on-write (page "生成一个字…", section

@@ -20,7 +20,8 @@ Pages the oracle follows (cited by title and section throughout):
   block mapping figure and the three innovations (section
   "PagedAttention 的破局哲学").
 * "第2章 KV Cache：模型内部的显存复用" -- 7B at 32K/128K vs weights
-  (section "拐点与结论").
+  (section "拐点与结论"); the radix-tree prefix cache of multi-turn
+  conversations (chapter summary, section 2.4).
 
 Modules
 -------
@@ -33,6 +34,9 @@ pool       bit-exact pool model: append (copy / FP8 quantise),
 attention  gather + fp64 textbook decode attention (GQA,
            window, FP8 dequant) and the split / log-sum-exp
            merge identity.                                     pinned
+prefix_cache  cached whole-block prefixes of token sequences,
+           LRU leaf eviction (the pages' radix-tree cache as a
+           plain set of prefixes).                             pinned
 
 Every function is pinned by tests under ``tests/`` marked ``not gpu``; no
 function here is "parity unpinned".
@@ -44,10 +48,11 @@ from .allocator import BlockManager, AllocatorError, OutOfBlocks
 from .pool import PoolModel, bits_to_f64
 from .attention import (decode_attention, gather_kv, partial_attention,
                         lse_merge, decode_attention_split)
+from .prefix_cache import PrefixCacheModel
 
 __all__ = [
     "kv_cache_bytes", "e4m3_decode_table", "e4m3_encode", "E4M3_MAX",
     "BlockManager", "AllocatorError", "OutOfBlocks", "PoolModel",
     "bits_to_f64", "decode_attention", "gather_kv", "partial_attention",
-    "lse_merge", "decode_attention_split",
+    "lse_merge", "decode_attention_split", "PrefixCacheModel",
 ]

@@ -217,6 +217,28 @@ class BlockManager:
             n += 1
         return n
 
+    # ---- references held outside tables (prefix cache) -------------------
+    def adopt(self, blocks, n_tokens: int) -> int:
+        """A new sequence whose table is `blocks` (each gains a holder) and
+        whose length is n_tokens, as a fork of a sequence holding exactly
+        those blocks would be."""
+        sid = self._next_id
+        self._next_id += 1
+        self._tables[sid] = [int(b) for b in blocks]
+        self._lens[sid] = int(n_tokens)
+        for b in self._tables[sid]:
+            self._ref[b] += 1
+        return sid
+
+    def ref_block(self, blk: int):
+        self._ref[blk] += 1
+
+    def unref_block(self, blk: int):
+        """One holder fewer; a block nobody holds goes to the back of the free queue."""
+        self._ref[blk] -= 1
+        if self._ref[blk] == 0:
+            self._free.append(blk)
+
     # ---- shared prefix ----------------------------------------------------
     def common_prefix(self, seqs) -> int:
         """Number of leading logical blocks that every sequence in seqs holds

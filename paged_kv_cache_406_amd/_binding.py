@@ -89,6 +89,12 @@ _SIGS = {
     "block_table_get": (c_i32, [P_pool, c_i32, P_i32, c_i32, P_i32, P_i32]),
     "block_table_export": (c_i32, [P_pool, c_vp, c_i32, c_i32, c_vp, c_vp]),
     "block_table_common_prefix": (c_i32, [P_pool, c_vp, c_i32, P_i32]),
+    "prefix_cache_create": (c_i32, [P_pool, ctypes.POINTER(c_vp)]),
+    "prefix_cache_destroy": (None, [c_vp]),
+    "prefix_cache_match": (c_i32, [c_vp, c_vp, c_i32, P_i32, P_i32]),
+    "prefix_cache_insert": (c_i32, [c_vp, c_i32, c_vp, c_i32]),
+    "prefix_cache_evict": (c_i32, [c_vp, c_i32, P_i32]),
+    "prefix_cache_stats": (c_i32, [c_vp, P_i32, P_i32]),
     "kv_pool_copy_blocks": (c_i32, [P_pool, c_vp, c_i32, c_vp]),
     "kv_metadata_upload": (c_i32, [c_vp, c_vp, c_size, c_vp]),
     "paged_kv_append": (c_i32, [P_pool, c_i32, c_vp, c_vp, c_i32, c_vp, c_i32, c_vp]),
@@ -295,6 +301,43 @@ def block_table_common_prefix(pool, seqs) -> int:
     out = c_i32()
     _check(_lib.block_table_common_prefix(pool, arr_p, len(arr), ctypes.byref(out)))
     return out.value
+
+
+# ---- prefix cache -------------------------------------------------------------
+def prefix_cache_create(pool) -> int:
+    h = c_vp()
+    _check(_lib.prefix_cache_create(pool, ctypes.byref(h)))
+    return h.value
+
+
+def prefix_cache_destroy(cache) -> None:
+    _lib.prefix_cache_destroy(cache)
+
+
+def prefix_cache_match(cache, tokens):
+    """Returns (new sequence id, matched tokens)."""
+    arr, p = _i32_addr(tokens)
+    seq, matched = c_i32(), c_i32()
+    _check(_lib.prefix_cache_match(cache, p, len(arr), ctypes.byref(seq), ctypes.byref(matched)))
+    return seq.value, matched.value
+
+
+def prefix_cache_insert(cache, seq, tokens) -> None:
+    arr, p = _i32_addr(tokens)
+    _check(_lib.prefix_cache_insert(cache, seq, p, len(arr)))
+
+
+def prefix_cache_evict(cache, n_blocks) -> int:
+    out = c_i32()
+    _check(_lib.prefix_cache_evict(cache, n_blocks, ctypes.byref(out)))
+    return out.value
+
+
+def prefix_cache_stats(cache):
+    """Returns (cached blocks, tree nodes)."""
+    a, b = c_i32(), c_i32()
+    _check(_lib.prefix_cache_stats(cache, ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
 
 
 # ---- device work ------------------------------------------------------------

@@ -43,14 +43,16 @@ def _run(cmd, verbose):
 def build(verbose: bool = False) -> str:
     hipcc = _hipcc()
     with tempfile.TemporaryDirectory(prefix="pkv_build_") as tmp:
-        host_o = os.path.join(tmp, "pool.o")
+        host_objs = []
+        for src in ("pool.cpp", "prefix_cache.cpp"):
+            obj = os.path.join(tmp, src.replace(".cpp", ".o"))
+            _run(["g++", *HOST_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+            host_objs.append(obj)
         dev_o = os.path.join(tmp, "kernels.o")
-        _run(["g++", *HOST_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, "pool.cpp"),
-              "-o", host_o], verbose)
         _run([hipcc, *HIP_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, "kernels.hip"),
               "-o", dev_o], verbose)
         tmp_lib = os.path.join(tmp, "libpagedkv.so")
-        _run([hipcc, *HIP_FLAGS, "-shared", host_o, dev_o, "-o", tmp_lib], verbose)
+        _run([hipcc, *HIP_FLAGS, "-shared", *host_objs, dev_o, "-o", tmp_lib], verbose)
         shutil.copyfile(tmp_lib, LIB + ".tmp")
         os.replace(LIB + ".tmp", LIB)
     return LIB

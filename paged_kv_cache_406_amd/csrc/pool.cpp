@@ -110,6 +110,24 @@ static void do_append(kv_pool* p, Sequence& s, int64_t n, int64_t* slots,
   s.len = start + n;
 }
 
+void block_ref(kv_pool* p, int32_t b) { p->refcount[b] += 1; }
+
+void block_unref(kv_pool* p, int32_t b) {
+  p->refcount[b] -= 1;
+  if (p->refcount[b] == 0) push_free(p, b);
+}
+
+int32_t adopt_sequence(kv_pool* p, const std::vector<int32_t>& blocks, int64_t len) {
+  Sequence s;
+  s.table = blocks;     // may throw: nothing changed yet
+  s.len = len;
+  const int32_t id = p->next_id;
+  p->seqs.emplace(id, std::move(s));
+  for (int32_t b : blocks) p->refcount[b] += 1;
+  p->next_id++;
+  return id;
+}
+
 }  // namespace pkv
 
 using namespace pkv;

@@ -42,4 +42,12 @@ void set_error(const std::string& msg);
 pkv_status fail(pkv_status code, const std::string& msg);
 int elem_bytes(int32_t dtype);
 
+// Block references held outside sequence tables (the prefix cache): one more
+// holder of block b; one fewer (back to the free queue at zero).
+void block_ref(kv_pool* p, int32_t b);
+void block_unref(kv_pool* p, int32_t b);
+// A new sequence holding `blocks` (one more reference each) with `len`
+// tokens; returns its id.  Caller checks ids are not exhausted.
+int32_t adopt_sequence(kv_pool* p, const std::vector<int32_t>& blocks, int64_t len);
+
 }  // namespace pkv
