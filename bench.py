@@ -275,6 +275,18 @@ def run(args):
     torch.cuda.synchronize()
     n_kernels = {}
     step_lens = {}
+    # A steady batch keeps its tables resident on the device: one full export
+    # and upload here, then paged_kv_append_step updates them with each token.
+    # The forked branches of the prefix workload change every step and are
+    # exported and uploaded every step.
+    resident = not prefix and not args.full_metadata
+    if resident:
+        buf, npb = ring[0]
+        for rep in reps:
+            P.block_table_export(rep.pool.handle, rep.seq_arr, mb, tables_out=npb[4 * B: 4 * B + B * mb].reshape(B, mb),
+                                 lens_out=npb[4 * B + B * mb:])
+            P.kv_metadata_upload(rep.meta, buf, meta_bytes, sptr)
+            torch.cuda.synchronize()
 
     def step(t, record):
         rep = reps[t % len(reps)]
@@ -298,18 +310,26 @@ def run(args):
             seqs = rep.seq_arr
             rep.lengths += 1
         _, cows = P.block_table_append_batch(h, seqs, slots_out=slots_np, cow_out=cows_np)
-        P.block_table_export(h, seqs, mb, tables_out=tables_np, lens_out=lens_np)
+        kd, vd, _ = steps[t]
+        if resident:
+            if len(cows):
+                raise RuntimeError("copy-on-write in a batch without forks")
+            # new K/V and the rows' tables and lengths in one kernel; the
+            # slots are read from the page-locked buffer
+            P.paged_kv_append_step(h, 0, kd, vd, w.src_dtype, buf, B, rep.d_tables, rep.d_lens, mb, sptr)
+        else:
+            P.block_table_export(h, seqs, mb, tables_out=tables_np, lens_out=lens_np)
         if shared0:
             # the blocks the batch holds in common, read once by the decode
             k = P.block_table_common_prefix(h, seqs)
             if k != shared0:
                 raise RuntimeError(f"common prefix {k} blocks, expected {shared0}")
             dec_args[t].shared_prefix_blocks = k
-        P.kv_metadata_upload(rep.meta, buf, meta_bytes, sptr)
-        if len(cows):
-            P.kv_pool_copy_blocks(h, rep.d_cows, len(cows), sptr)
-        kd, vd, _ = steps[t]
-        P.paged_kv_append(h, 0, kd, vd, w.src_dtype, rep.d_slots, B, sptr)
+        if not resident:
+            P.kv_metadata_upload(rep.meta, buf, meta_bytes, sptr)
+            if len(cows):
+                P.kv_pool_copy_blocks(h, rep.d_cows, len(cows), sptr)
+            P.paged_kv_append(h, 0, kd, vd, w.src_dtype, rep.d_slots, B, sptr)
         if t in sampled:
             n_kernels[t] = P.paged_attention_decode_timed(h, dec_args[t], sampled[t], sptr)
         else:
@@ -355,6 +375,14 @@ def run(args):
     b1.record(stream)
     torch.cuda.synchronize()
     b2b_ms = b0.elapsed_time(b1) / n_b2b
+    if resident:
+        # the resident tables must still equal the host block manager's
+        for rep in reps:
+            ht, hl = P.block_table_export(rep.pool.handle, rep.seq_arr, mb)
+            dt = rep.d_tables.view(B, mb).cpu().numpy()
+            dl = rep.d_lens.cpu().numpy()
+            if not (np.array_equal(dt, ht) and np.array_equal(dl, hl)):
+                raise RuntimeError("device-resident block tables differ from the host block manager")
     b2b_bytes = float(np.mean([unique_or_logical([step_lens[order[k % len(order)]]])[1] for k in range(n_b2b)]))
     gc.enable()
     gc.unfreeze()
@@ -399,6 +427,8 @@ def run(args):
             "head_dim": w.head_dim, "block_size": w.block_size, "kv_dtype": w.kv_dtype,
             "mean_context": float(np.mean(d.lengths)), "sliding_window": w.window,
             "num_splits": args.splits, "replicas": len(reps), "shared_prefix_blocks": shared0,
+            "metadata": ("device-resident tables updated by paged_kv_append_step" if resident
+                         else "tables exported and uploaded every step"),
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "seq_heads_per_s": round(B * w.num_q_heads / (step_ms * 1e-3), 1),
@@ -535,6 +565,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--full-metadata", action="store_true",
+                    help="export and upload every step's tables instead of keeping them resident")
     ap.add_argument("--no-shared-prefix", action="store_true",
                     help="decode forked families without reading their common prefix once")
     ap.add_argument("--traffic", type=float, default=None,

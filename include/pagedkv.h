@@ -284,6 +284,27 @@ pkv_status paged_kv_append(kv_pool* pool, int32_t layer, const void* d_k, const 
                            int32_t src_dtype, const int64_t* d_slots, int32_t n_tokens,
                            pkv_stream stream);
 
+/* One decode step of a batch whose tables are resident on the device: row
+ * i (0 <= i < n) gets one new token, the token of slots[i] (from
+ * block_table_append_batch over the batch's sequences in row order).  Its K
+ * and V are written as paged_kv_append writes them, and the same kernel
+ * brings the row's metadata up to date: d_tables[i][d_lens[i] / block_size]
+ * = slots[i] / block_size (a new block, or the block a copy-on-write made),
+ * then d_lens[i] += 1 -- exactly the host block manager's table and length,
+ * without exporting and uploading the whole tables each step (a4 done in
+ * place; page "AI 陪读顶会论文（三）", section "PagedAttention 的破局哲学").
+ * d_tables: device int32 [n][max_blocks], d_lens: device int32 [n], both
+ * equal to the host state before the step (upload them once, e.g. with
+ * block_table_export + kv_metadata_upload).  slots: int64 [n] in device
+ * memory or in page-locked host memory (read directly by the kernel; keep it
+ * unchanged until the step has run).  Copy-on-write pairs of the step must be
+ * copied (kv_pool_copy_blocks) before.  A slot outside the pool, or a
+ * position at or past max_blocks * block_size, leaves that row unchanged.
+ * PKV_E_INVAL when a pointer does not lie in a suitable allocation. */
+pkv_status paged_kv_append_step(kv_pool* pool, int32_t layer, const void* d_k, const void* d_v,
+                                int32_t src_dtype, const int64_t* slots, int32_t n, int32_t* d_tables,
+                                int32_t* d_lens, int32_t max_blocks, pkv_stream stream);
+
 typedef struct {
   int32_t layer;
   int32_t batch;                /* B >= 0 */

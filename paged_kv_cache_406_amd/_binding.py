@@ -98,6 +98,7 @@ _SIGS = {
     "kv_pool_copy_blocks": (c_i32, [P_pool, c_vp, c_i32, c_vp]),
     "kv_metadata_upload": (c_i32, [c_vp, c_vp, c_size, c_vp]),
     "paged_kv_append": (c_i32, [P_pool, c_i32, c_vp, c_vp, c_i32, c_vp, c_i32, c_vp]),
+    "paged_kv_append_step": (c_i32, [P_pool, c_i32, c_vp, c_vp, c_i32, c_vp, c_i32, c_vp, c_vp, c_i32, c_vp]),
     "paged_attention_workspace_size": (c_i32, [P_pool, ctypes.POINTER(paged_decode_args), ctypes.POINTER(c_size)]),
     "paged_attention_decode": (c_i32, [P_pool, ctypes.POINTER(paged_decode_args), c_vp]),
     "paged_attention_decode_timed": (c_i32, [P_pool, ctypes.POINTER(paged_decode_args), c_vp,
@@ -354,6 +355,15 @@ def kv_metadata_upload(d_dst, h_src, nbytes, stream=None) -> None:
 def paged_kv_append(pool, layer, d_k, d_v, src_dtype, d_slots, n_tokens, stream=None) -> None:
     _check(_lib.paged_kv_append(pool, layer, _ptr(d_k), _ptr(d_v), DTYPE_CODE.get(src_dtype, src_dtype),
                                 _ptr(d_slots), n_tokens, _stream(stream)))
+
+
+def paged_kv_append_step(pool, layer, d_k, d_v, src_dtype, slots, n, d_tables, d_lens, max_blocks,
+                         stream=None) -> None:
+    """One token per row 0..n-1, with the rows' device tables and lengths
+    updated in the same kernel.  slots: device tensor, pinned host tensor, or
+    an address."""
+    _check(_lib.paged_kv_append_step(pool, layer, _ptr(d_k), _ptr(d_v), DTYPE_CODE.get(src_dtype, src_dtype),
+                                     _ptr(slots), n, _ptr(d_tables), _ptr(d_lens), max_blocks, _stream(stream)))
 
 
 def make_decode_args(layer, batch, num_q_heads, max_blocks_per_seq, q, q_dtype, block_tables,

@@ -142,6 +142,12 @@ struct AppendParams {
   const float* v_inv;
   int64_t num_blocks;
   int32_t n, hkv, d, bs, layer;
+  // step mode (tables != NULL): token i is row i's next token; its block
+  // goes into tables[i][lens[i] / bs] and lens[i] grows by one, and the slots
+  // may be in page-locked host memory (read with system-scope loads)
+  int32_t* tables;
+  int32_t* lens;
+  int32_t max_blocks;
 };
 
 template <int KV, int SRC>
@@ -155,10 +161,20 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams P) {
   const int c = (int)(t % chunks);
   const int h = (int)((t / chunks) % P.hkv);
   const int64_t i = t / ((int64_t)chunks * P.hkv);
-  const int64_t slot = P.slots[i];
+  const int64_t slot = P.tables ? __hip_atomic_load(P.slots + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)
+                                : P.slots[i];
   if (slot < 0 || slot >= P.num_blocks * P.bs) return;
   const int64_t blk = slot / P.bs;
   const int off = (int)(slot % P.bs);
+  if (P.tables && h == 0 && c == 0) {
+    // the row's table and length follow the host block manager's decision,
+    // which the slot encodes: block slot / bs at position lens[i]
+    const int32_t pos = P.lens[i];
+    if (pos >= 0 && pos / P.bs < P.max_blocks) {
+      P.tables[i * P.max_blocks + pos / P.bs] = (int32_t)blk;
+      P.lens[i] = pos + 1;
+    }
+  }
   const int64_t tile = ((int64_t)P.layer * P.num_blocks + blk) * P.hkv + h;
   const int64_t src0 = (i * P.hkv + h) * P.d + (int64_t)c * X;  // element index
   uint8_t* kdst = P.kc + ((tile * (P.d / X) + c) * P.bs + off) * 16;
@@ -1581,9 +1597,9 @@ pkv_status kv_metadata_upload(void* d_dst, const void* h_src, size_t bytes, pkv_
   return e == hipSuccess ? PKV_OK : hip_fail(e, "upload launch");
 }
 
-pkv_status paged_kv_append(kv_pool* pool, int32_t layer, const void* d_k, const void* d_v,
-                           int32_t src_dtype, const int64_t* d_slots, int32_t n_tokens,
-                           pkv_stream stream) {
+static pkv_status append_launch(kv_pool* pool, int32_t layer, const void* d_k, const void* d_v,
+                                int32_t src_dtype, const int64_t* d_slots, int32_t n_tokens, int32_t* d_tables,
+                                int32_t* d_lens, int32_t max_blocks, pkv_stream stream) {
   if (!pool || n_tokens < 0) return fail(PKV_E_INVAL, "bad argument");
   const kv_pool_desc& d = pool->desc;
   if (!d.k_cache || !d.v_cache) return fail(PKV_E_INVAL, "pool has no device buffers");
@@ -1610,6 +1626,9 @@ pkv_status paged_kv_append(kv_pool* pool, int32_t layer, const void* d_k, const 
   P.d = d.head_dim;
   P.bs = d.block_size;
   P.layer = layer;
+  P.tables = d_tables;
+  P.lens = d_lens;
+  P.max_blocks = max_blocks;
   const int X = 16 / elem_bytes(d.kv_dtype);
   const int64_t total = (int64_t)n_tokens * d.num_kv_heads * (d.head_dim / X);
   const int64_t blocks = (total + 255) / 256;
@@ -1634,6 +1653,34 @@ pkv_status paged_kv_append(kv_pool* pool, int32_t layer, const void* d_k, const 
   hipLaunchKernelGGL(fn, dim3((uint32_t)blocks), dim3(256), 0, (hipStream_t)stream, P);
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? PKV_OK : hip_fail(e, "append launch");
+}
+
+pkv_status paged_kv_append(kv_pool* pool, int32_t layer, const void* d_k, const void* d_v,
+                           int32_t src_dtype, const int64_t* d_slots, int32_t n_tokens,
+                           pkv_stream stream) {
+  return append_launch(pool, layer, d_k, d_v, src_dtype, d_slots, n_tokens, nullptr, nullptr, 0, stream);
+}
+
+pkv_status paged_kv_append_step(kv_pool* pool, int32_t layer, const void* d_k, const void* d_v,
+                                int32_t src_dtype, const int64_t* slots, int32_t n, int32_t* d_tables,
+                                int32_t* d_lens, int32_t max_blocks, pkv_stream stream) {
+  if (n > 0 && (!d_tables || !d_lens || !slots)) return fail(PKV_E_INVAL, "null pointer");
+  if (max_blocks <= 0) return fail(PKV_E_INVAL, "max_blocks must be positive");
+  if (n <= 0) return n < 0 ? fail(PKV_E_INVAL, "bad argument") : PKV_OK;
+  const size_t sb = (size_t)n * sizeof(int64_t);
+  const int64_t* dev_slots = slots;
+  if (in_one_allocation(slots, sb, hipMemoryTypeHost)) {
+    hipPointerAttribute_t at;
+    hipError_t e = hipPointerGetAttributes(&at, slots);
+    if (e != hipSuccess || !at.devicePointer) return hip_fail(e, "hipPointerGetAttributes");
+    dev_slots = static_cast<const int64_t*>(at.devicePointer);
+  } else if (!in_one_allocation(slots, sb, hipMemoryTypeDevice)) {
+    return fail(PKV_E_INVAL, "slots must lie in one device or page-locked host allocation");
+  }
+  if (!in_one_allocation(d_tables, (size_t)n * max_blocks * sizeof(int32_t), hipMemoryTypeDevice) ||
+      !in_one_allocation(d_lens, (size_t)n * sizeof(int32_t), hipMemoryTypeDevice))
+    return fail(PKV_E_INVAL, "tables and lengths must lie in device allocations of [n][max_blocks] and [n]");
+  return append_launch(pool, layer, d_k, d_v, src_dtype, dev_slots, n, d_tables, d_lens, max_blocks, stream);
 }
 
 pkv_status paged_attention_workspace_size(const kv_pool* pool, const paged_decode_args* a, size_t* bytes_out) {
