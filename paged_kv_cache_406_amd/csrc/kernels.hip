@@ -255,7 +255,20 @@ struct DecodeParams {
   int32_t pre_chunks; // token chunks of the prefix
   int32_t pre_rtiles; // query-row groups (one workgroup each) per KV head
   float* ws_pre;      // [pre_chunks + 1][B * Hq][D + 4]: o, max, sum, 2 pad
+  // range mode: results of pieces that end before a wavefront's range does
+  // are kept in LDS (up to `nstage` per wavefront, from byte `stage_off` of
+  // the dynamic LDS block) and written when the range is done
+  int32_t nstage;
+  int32_t stage_off;
 };
+
+// Which piece an LDS staging slot of the decode holds (48 bytes, so that
+// slots and wavefront areas stay 16-byte aligned).
+struct PieceTag {
+  int32_t g, b, nb, pad;
+  int64_t start, beg, end, pad2;
+};
+static_assert(sizeof(PieceTag) == 48, "staging tag layout");
 
 // Tokens per sub-tile: the amount one wavefront loads and scores at a time.
 // Each lane group (16 lanes) holds TT/4 consecutive tokens of V, which is
@@ -459,33 +472,32 @@ struct Decoder {
     float l;
   };
 
-  // q operands of head i of group g (zero for i >= G).  Element e of operand
-  // s multiplies the same channel as element e of the K operand of step s.
-  // FP8 folds the per-channel K scale into q (q'[c] = q[c] * k_scale[c]).
+  // q operands of head i of group g.  Element e of operand s multiplies the
+  // same channel as element e of the K operand of step s.  FP8 folds the
+  // per-channel K scale into q (q'[c] = q[c] * k_scale[c]).  Lanes i >= G
+  // (MFMA columns whose results are never written) read head 0's row.
   static __device__ __forceinline__ void load_q(const DecodeParams& P, int b, int g, int i, int kg,
                                                 qop (&qo)[NQ]) {
-    const bool live = i < P.group;
-    load_q_at(P, g, ((int64_t)b * P.hq + (int64_t)g * P.group + (live ? i : 0)) * D, live, kg, qo);
+    load_q_at(P, g, ((int64_t)b * P.hq + (int64_t)g * P.group + (i < P.group ? i : 0)) * D, kg, qo);
   }
 
   // Query row (element offset `row` of q, a head of KV head g) as this lane's
-  // MFMA column; zeros when !live.
-  static __device__ __forceinline__ void load_q_at(const DecodeParams& P, int g, int64_t row, bool live, int kg,
+  // MFMA column.  The row must exist; the caller points the lanes of unused
+  // columns at a real row.  Nothing is selected after the loads, so the wait
+  // for them falls where the operands are first used, not here (the stream
+  // prefetches the next piece's queries a sub-tile early).
+  static __device__ __forceinline__ void load_q_at(const DecodeParams& P, int g, int64_t row, int kg,
                                                    qop (&qo)[NQ]) {
     if constexpr (KV == KV_F32) {
       const float* q = reinterpret_cast<const float*>(P.q) + row;
 #pragma unroll
       for (int j = 0; j < NKJ; ++j)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) qo[4 * j + u] = live ? q[(kg + 4 * j) * 4 + u] : 0.0f;
+        for (int u = 0; u < 4; ++u) qo[4 * j + u] = q[(kg + 4 * j) * 4 + u];
     } else if constexpr (KV == KV_F16 || KV == KV_BF16) {
       const uint8_t* q = P.q + row * 2;
 #pragma unroll
-      for (int j = 0; j < NKJ; ++j) {
-        uint4 w = *reinterpret_cast<const uint4*>(q + (kg + 4 * j) * 16);
-        if (!live) w = make_uint4(0, 0, 0, 0);
-        qo[j] = as8<qop>(w);
-      }
+      for (int j = 0; j < NKJ; ++j) qo[j] = as8<qop>(*reinterpret_cast<const uint4*>(q + (kg + 4 * j) * 16));
     } else {
       const uint16_t* q = reinterpret_cast<const uint16_t*>(P.q) + row;
       const float* ks = P.k_scale + ((int64_t)P.layer * P.hkv + g) * D;
@@ -497,8 +509,8 @@ struct Decoder {
 #pragma unroll
           for (int e = 0; e < 8; e += 2) {
             const int c = (kg + 4 * j) * 16 + 8 * h + e;
-            const float x0 = live ? bf16_bits_to_f32(q[c]) * ks[c] : 0.0f;
-            const float x1 = live ? bf16_bits_to_f32(q[c + 1]) * ks[c + 1] : 0.0f;
+            const float x0 = bf16_bits_to_f32(q[c]) * ks[c];
+            const float x1 = bf16_bits_to_f32(q[c + 1]) * ks[c + 1];
             w[e / 2] = f32_to_bf16_bits_rne(x0) | (f32_to_bf16_bits_rne(x1) << 16);
           }
           qo[2 * j + h] = as8<qop>(make_uint4(w[0], w[1], w[2], w[3]));
@@ -856,6 +868,57 @@ struct Decoder {
     }
   }
 
+  // LDS staging of a finished piece.  A wavefront's area holds `nstage`
+  // slots, then one PieceTag per slot.  Slot layout, npos = 4G positions
+  // (lane (i, kg), i < G, at position kg * G + i): o as [NV][npos] 16-byte
+  // groups (consecutive lanes 16 bytes apart), then (max, sum) as [npos].
+  static __host__ __device__ constexpr int stage_slot_bytes(int G) { return 4 * G * (D + 8); }
+  static __host__ __device__ constexpr int stage_area_bytes(int G, int nstage) {
+    return nstage * (stage_slot_bytes(G) + (int)sizeof(PieceTag));
+  }
+
+  static __device__ __forceinline__ void stage_put(uint8_t* area, int nstage, int k, int G, const State& st,
+                                                   const Seg& s, int64_t beg, int64_t end, int i, int kg,
+                                                   int lane) {
+    const int npos = 4 * G;
+    uint8_t* slot = area + k * stage_slot_bytes(G);
+    if (i < G) {
+      const int pos = kg * G + i;
+#pragma unroll
+      for (int n = 0; n < NV; ++n) *reinterpret_cast<f32x4*>(slot + (n * npos + pos) * 16) = st.O[n];
+      *reinterpret_cast<f32x2*>(slot + npos * D + pos * 8) = f32x2{st.m, st.l};
+    }
+    if (lane == 0) {
+      PieceTag* t = reinterpret_cast<PieceTag*>(area + nstage * stage_slot_bytes(G)) + k;
+      t->g = s.g;
+      t->b = s.b;
+      t->nb = s.nb;
+      t->start = s.start;
+      t->beg = beg;
+      t->end = end;
+    }
+  }
+
+  static __device__ __forceinline__ void stage_get(const uint8_t* area, int nstage, int k, int G, State& st,
+                                                   Seg& s, int64_t* beg, int64_t* end, int i, int kg) {
+    const int npos = 4 * G;
+    const uint8_t* slot = area + k * stage_slot_bytes(G);
+    const int pos = i < G ? kg * G + i : 0;
+#pragma unroll
+    for (int n = 0; n < NV; ++n) st.O[n] = *reinterpret_cast<const f32x4*>(slot + (n * npos + pos) * 16);
+    const f32x2 ml = *reinterpret_cast<const f32x2*>(slot + npos * D + pos * 8);
+    st.m = ml[0];
+    st.l = ml[1];
+    const PieceTag* t = reinterpret_cast<const PieceTag*>(area + nstage * stage_slot_bytes(G)) + k;
+    s.g = uniform(t->g);
+    s.b = uniform(t->b);
+    s.nb = uniform(t->nb);
+    s.start = uniform(t->start);
+    s.L = s.lo = s.first = 0;
+    *beg = uniform(t->beg);
+    *end = uniform(t->end);
+  }
+
   // Query-row tiles (MFMA column blocks of 16 rows) per wavefront of prefix_kernel.
   static constexpr int NT = 2;
   // 16-byte K and V groups of one sub-tile: one per lane per load of load_k /
@@ -896,7 +959,7 @@ struct Decoder {
       const int b = live[t] ? (int)(r / G) : 0;
       const int hg = live[t] ? (int)(r % G) : 0;
       hrow[t] = (int64_t)b * P.hq + (int64_t)g * G + hg;
-      load_q_at(P, g, hrow[t] * D, live[t], kg, q[t]);
+      load_q_at(P, g, hrow[t] * D, kg, q[t]);
       int32_t L = P.lens[b];
       L = L < 0 ? 0 : (L > cap ? cap : L);
       Lc[t] = live[t] ? min(L, kT) : 0;
@@ -1020,7 +1083,7 @@ struct Decoder {
   // piece streams.  C: unit prefix sums (NULL in single mode, where the range
   // is the whole of one pair).
   static __device__ void stream(const DecodeParams& P, const int32_t* C, int64_t t_head, int64_t T, int64_t W,
-                                int64_t w, int64_t r0, int64_t r1, int g0, int b0) {
+                                int64_t w, int64_t r0, int64_t r1, int g0, int b0, uint8_t* stage) {
     const int lane = threadIdx.x & 63;
     const int i = lane & 15;
     const int kg = lane >> 4;
@@ -1099,9 +1162,14 @@ struct Decoder {
     };
     reset();
     // after the last sub-tile of a piece: write it, then take over the piece
-    // the loads have moved on to
+    // the loads have moved on to.  While the range goes on, the piece's
+    // result is kept in LDS when there is room: a store issued now would sit
+    // in the same in-order wait counter as the loads in flight, and the next
+    // waits for sub-tiles would also wait for its acknowledgement.
+    int nst = 0;
     auto step_piece = [&](bool more) {
-      finish(P, st, cs, cbeg, cend, r0, T, W, w, i, kg, lane);
+      if (more && nst < P.nstage) stage_put(stage, P.nstage, nst++, P.group, st, cs, cbeg, cend, i, kg, lane);
+      else finish(P, st, cs, cbeg, cend, r0, T, W, w, i, kg, lane);
       if (more) {
         cs = ls;
         cbeg = lbeg;
@@ -1120,7 +1188,8 @@ struct Decoder {
     f32x4 S[NQT];
     float p[NQT][4];
     bool last0, last1;
-    Addr a0 = where(last0), a1;
+    Addr a0 = where(last0);
+    Addr a1 = a0;
     load_k(K0, a0);
     load_v(V0, a0);
     // sched_barrier keeps the compiler from hoisting the next sub-tile's
@@ -1128,34 +1197,37 @@ struct Decoder {
     // at once and spill).
     for (int64_t s = 0; s < nsub; s += 2) {
       const bool n1 = s + 1 < nsub;
-      if (n1) {
-        a1 = where(last1);
-        load_k(K1, a1);
-      }
+      if (n1) a1 = where(last1);
+      load_k(K1, a1);
       __builtin_amdgcn_sched_barrier(0);
       qk(K0, q, S);
       softmax(V0, S, st, p, cs.lo, cs.L, P.scale_log2, kg);
       __builtin_amdgcn_sched_barrier(0);
-      if (n1) load_v(V1, a1);
+      load_v(V1, a1);
       __builtin_amdgcn_sched_barrier(0);
       pv(V0, p, st, cs.lo, cs.L, kg);
       __builtin_amdgcn_sched_barrier(0);
       if (last0) step_piece(n1);
       if (!n1) break;
       const bool n2 = s + 2 < nsub;
-      if (n2) {
-        a0 = where(last0);
-        load_k(K0, a0);
-      }
+      if (n2) a0 = where(last0);
+      load_k(K0, a0);
       __builtin_amdgcn_sched_barrier(0);
       qk(K1, q, S);
       softmax(V1, S, st, p, cs.lo, cs.L, P.scale_log2, kg);
       __builtin_amdgcn_sched_barrier(0);
-      if (n2) load_v(V0, a0);
+      load_v(V0, a0);
       __builtin_amdgcn_sched_barrier(0);
       pv(V1, p, st, cs.lo, cs.L, kg);
       __builtin_amdgcn_sched_barrier(0);
       if (last1) step_piece(n2);
+    }
+    // the staged pieces, now that no load is in flight
+    for (int k = 0; k < nst; ++k) {
+      Seg ps;
+      int64_t pbeg, pend;
+      stage_get(stage, P.nstage, k, P.group, st, ps, &pbeg, &pend, i, kg);
+      finish(P, st, ps, pbeg, pend, r0, T, W, w, i, kg, lane);
     }
   }
 };
@@ -1182,7 +1254,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       write_zero_rows<D>(P, b, g, lane);
       return;
     }
-    Dec::stream(P, nullptr, 0, 0, 0, 0, 0, 0, g, b);
+    Dec::stream(P, nullptr, 0, 0, 0, 0, 0, 0, g, b, nullptr);
     return;
   }
 
@@ -1217,7 +1289,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       if (C[mid] <= r) lo_b = mid;
       else hi_b = mid - 1;
     }
-    Dec::stream(P, C, t_head, T, W, w, r0, r1, g, uniform(lo_b));
+    uint8_t* stage = reinterpret_cast<uint8_t*>(C) + P.stage_off + wid * Dec::stage_area_bytes(P.group, P.nstage);
+    Dec::stream(P, C, t_head, T, W, w, r0, r1, g, uniform(lo_b), stage);
   }
 }
 
@@ -1744,6 +1817,8 @@ static pkv_status decode_launch(const kv_pool* pool, const paged_decode_args* a,
   P.ws_job = nullptr;
   P.ws_pre = nullptr;
   P.xcd_remap = 0;
+  P.nstage = 0;
+  P.stage_off = 0;
   P.shared = a->shared_prefix_blocks;
   P.pre_chunks = 0;
   P.pre_rtiles = 0;
@@ -1801,7 +1876,12 @@ static pkv_status decode_launch(const kv_pool* pool, const paged_decode_args* a,
   int64_t grid = (W + 3) / 4;
   grid = ((grid + 7) / 8) * 8;  // whole rounds over the 8 XCDs
   P.xcd_remap = 1;
-  const size_t lds = (size_t)(a->batch + 1) * sizeof(int32_t);
+  // unit prefix sums, then as many staging slots per wavefront (at most 4)
+  // as fit in 64 KiB
+  P.stage_off = (int32_t)(((a->batch + 1) * (int64_t)sizeof(int32_t) + 15) / 16 * 16);
+  const int64_t per_slot = 4 * (int64_t)(4 * P.group * (d.head_dim + 8) + (int64_t)sizeof(PieceTag));
+  P.nstage = (int32_t)std::max<int64_t>(0, std::min<int64_t>(4, (65536 - P.stage_off) / per_slot));
+  const size_t lds = (size_t)P.stage_off + (size_t)P.nstage * per_slot;
   e = launch(fn, dim3((uint32_t)grid), lds, s, ev_first, ev ? ev[1] : nullptr, P);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   if (nk) *nk = 1;
