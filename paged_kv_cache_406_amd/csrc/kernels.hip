@@ -1877,10 +1877,10 @@ static pkv_status decode_launch(const kv_pool* pool, const paged_decode_args* a,
   grid = ((grid + 7) / 8) * 8;  // whole rounds over the 8 XCDs
   P.xcd_remap = 1;
   // unit prefix sums, then as many staging slots per wavefront (at most 4)
-  // as fit in 64 KiB
+  // as fit, with the static LDS, in 64 KiB
   P.stage_off = (int32_t)(((a->batch + 1) * (int64_t)sizeof(int32_t) + 15) / 16 * 16);
   const int64_t per_slot = 4 * (int64_t)(4 * P.group * (d.head_dim + 8) + (int64_t)sizeof(PieceTag));
-  P.nstage = (int32_t)std::max<int64_t>(0, std::min<int64_t>(4, (65536 - P.stage_off) / per_slot));
+  P.nstage = (int32_t)std::max<int64_t>(0, std::min<int64_t>(4, (63488 - P.stage_off) / per_slot));
   const size_t lds = (size_t)P.stage_off + (size_t)P.nstage * per_slot;
   e = launch(fn, dim3((uint32_t)grid), lds, s, ev_first, ev ? ev[1] : nullptr, P);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
