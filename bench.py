@@ -13,9 +13,14 @@ timed region starts.  Several independently placed copies of the cache are
 rotated so the working set is several times the 256 MB Infinity Cache.
 
 Prints one JSON line.  ``value`` is KV GB/s over the whole step (algorithmic
-bytes of the decode / step time); ``roofline`` is the decode call alone,
-timed with events on the launch stream; ``cpu_baseline`` is the CPU oracle
-timed on a bounded sample of the same workload.
+bytes of the decode / step time).  ``roofline`` is the dominant kernel,
+decode_kernel, alone: its algorithmic bytes (everything the call must move
+except the output, which the merge writes) over its own launch duration,
+recorded by the kernel's start and end events on the launch stream;
+``decode_ms`` / ``decode_GBps`` are the whole call (decode_kernel +
+merge_kernel).  With a shared prefix the three kernels of the call are one
+unit and ``roofline`` is the call.  ``cpu_baseline`` is the CPU oracle timed
+on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload c3]
 """
@@ -50,14 +55,14 @@ WORKLOAD_NAMES = {
 }
 
 
-# HBM bytes per paged_attention_decode call (decode_kernel + merge_kernel, read +
-# write), from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs scaled by what the
-# same counters read for a plain 1 GiB device copy (FETCH x 2.0, WRITE x 1.0).
-# Each entry holds for the kernel source it was measured on (kernels_sha());
-# for any other source the figure is not reported.
+# HBM bytes per decode_kernel launch (read + write), from rocprofv3 --pmc
+# FETCH_SIZE and WRITE_SIZE runs scaled by what the same counters read for a
+# plain 1 GiB device copy (FETCH x 2.0, WRITE x 1.0).  Each entry holds for the
+# kernel source it was measured on (kernels_sha()); for any other source the
+# figure is not reported.
 MEASURED_TRAFFIC = {
-    "c3": (517.2e6, "1c5c2f84866e8e0a"),
-    "c5": (2158.8e6, "1c5c2f84866e8e0a"),
+    "c3": (506.5e6, "bc599b351fff673a"),
+    "c5": (2154.5e6, "bc599b351fff673a"),
 }
 
 
@@ -84,6 +89,12 @@ def unique_kv_bytes(w, lengths):
     eb = wl.ELEM_BYTES[w.kv_dtype]
     per_tok = w.num_kv_heads * 2 * w.head_dim * eb
     return (w.prefix_len + sum(int(L) - w.prefix_len for L in lengths)) * per_tok
+
+
+def out_bytes(w, lengths):
+    """The fp32 output of one decode call (written by merge_kernel for split
+    sequences)."""
+    return len(lengths) * w.num_q_heads * w.head_dim * 4
 
 
 def decode_bytes(w, lengths):
@@ -387,13 +398,16 @@ def run(args):
     gc.enable()
     gc.unfreeze()
     timed = [t for t in range(args.warmup, args.warmup + args.steps) if t in sampled]
-    dec_ms = []
+    dec_ms = []      # the call: every kernel's duration
+    kern_ms = []     # decode_kernel (with a shared prefix: prefix_kernel start to decode_kernel end)
     for t in timed:
         e = sampled[t]
-        ms = e[0].elapsed_time(e[1])
+        k0 = e[0].elapsed_time(e[1])
+        ms = k0
         if n_kernels[t] == 2:
             ms += e[2].elapsed_time(e[3])
         dec_ms.append(ms)
+        kern_ms.append(k0)
     step_ms = t_start.elapsed_time(t_stop) / args.steps
     all_lens = [step_lens[t] for t in range(args.warmup, args.warmup + args.steps)]
     avg_dec_ms = float(np.mean(dec_ms))
@@ -401,13 +415,22 @@ def run(args):
     logical_bytes, avg_bytes = unique_or_logical(all_lens)          # the whole timed region
     s_logical, s_bytes = unique_or_logical([step_lens[t] for t in timed])   # the sampled decodes
     log(f"step {step_ms:.4f} ms (host wall {1e3 * wall / args.steps:.4f} ms), decode kernels {avg_dec_ms:.4f} ms "
-        f"(min {min(dec_ms):.4f}, max {max(dec_ms):.4f}, {len(dec_ms)} sampled steps), back to back "
-        f"{b2b_ms:.4f} ms")
+        f"(min {min(dec_ms):.4f}, max {max(dec_ms):.4f}, {len(dec_ms)} sampled steps; first kernel "
+        f"{float(np.mean(kern_ms)):.4f} ms), back to back {b2b_ms:.4f} ms")
     value = avg_bytes / (step_ms * 1e-3) / 1e9
     traffic = args.traffic * 1e9 if args.traffic else None
     if traffic is None and w.name in MEASURED_TRAFFIC and MEASURED_TRAFFIC[w.name][1] == kernels_sha():
         traffic = MEASURED_TRAFFIC[w.name][0]
     achieved = s_bytes / (avg_dec_ms * 1e-3) / 1e9
+    avg_kern_ms = float(np.mean(kern_ms))
+    if prefix:
+        # prefix, suffix and merge kernels work as one: the roofline is the call
+        r_kernel, r_ms, r_bytes = ("paged_attention_decode (prefix_kernel + decode_kernel + merge_kernel)",
+                                   avg_dec_ms, s_bytes)
+    else:
+        s_out = float(np.mean([out_bytes(w, step_lens[t]) for t in timed]))
+        r_kernel, r_ms, r_bytes = "decode_kernel", avg_kern_ms, s_bytes - s_out
+    r_achieved = r_bytes / (r_ms * 1e-3) / 1e9
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -437,16 +460,18 @@ def run(args):
         "decode_seq_heads_per_s": round(B * w.num_q_heads / (avg_dec_ms * 1e-3), 1),
         "roofline": {
             "bound": "hbm",
-            "achieved": round(achieved, 2),
+            "achieved": round(r_achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "frac": round(r_achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "paged_attention_decode (" + ("prefix_kernel + " if shared0 else "")
-                      + "decode_kernel + merge_kernel)",
+            "kernel": r_kernel,
+            "launch_ms": round(r_ms, 5),
+            "algorithmic_bytes": round(r_bytes),
         },
-        "decode_timing": f"sum of the call's kernel durations, recorded by the kernels themselves "
-                         f"(hipExtLaunchKernelGGL events) on {len(dec_ms)} of the {args.steps} timed steps",
+        "decode_timing": f"kernel durations recorded by the kernels themselves (hipExtLaunchKernelGGL "
+                         f"start and end events) on {len(dec_ms)} of the {args.steps} timed steps; "
+                         f"decode_ms sums the call's kernels",
         "decode_back_to_back_ms": round(b2b_ms, 5),
         "decode_back_to_back_GBps": round(b2b_bytes / (b2b_ms * 1e-3) / 1e9, 2),
         "cpu_baseline": None,
@@ -570,7 +595,7 @@ def main():
     ap.add_argument("--no-shared-prefix", action="store_true",
                     help="decode forked families without reading their common prefix once")
     ap.add_argument("--traffic", type=float, default=None,
-                    help="HBM bytes per decode call from rocprofv3 counters (GB)")
+                    help="HBM bytes per decode_kernel launch from rocprofv3 counters (GB)")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
     args = ap.parse_args()

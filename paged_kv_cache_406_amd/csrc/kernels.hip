@@ -260,6 +260,9 @@ struct DecodeParams {
   // the dynamic LDS block) and written when the range is done
   int32_t nstage;
   int32_t stage_off;
+  // range mode: 1 when the context lengths are also kept in LDS, after the
+  // unit prefix sums (a piece's start then reads no global memory)
+  int32_t lens_in_lds;
 };
 
 // Which piece an LDS staging slot of the decode holds (48 bytes, so that
@@ -289,9 +292,8 @@ struct Units {
 // Attended range of sequence b: L tokens (clamped to the table), first key
 // lo (window), first block, and the number of work units from that block on.
 template <int BS, int U>
-__device__ __forceinline__ void seq_extent(const DecodeParams& P, int b, int32_t* L_out, int32_t* lo_out,
-                                           int32_t* first_out, int32_t* nunits_out) {
-  int32_t L = P.lens[b];
+__device__ __forceinline__ void extent_of(const DecodeParams& P, int32_t L, int32_t* L_out, int32_t* lo_out,
+                                          int32_t* first_out, int32_t* nunits_out) {
   const int32_t cap = P.max_blocks * BS;
   L = L < 0 ? 0 : (L > cap ? cap : L);
   const int32_t lo = P.window > 0 ? (L - P.window > 0 ? L - P.window : 0) : 0;
@@ -304,7 +306,14 @@ __device__ __forceinline__ void seq_extent(const DecodeParams& P, int b, int32_t
   *nunits_out = L > lo && L > first * BS ? (L - first * BS + U - 1) / U : 0;
 }
 
-// Exclusive prefix sums of the per-sequence unit counts into C[0..B] (LDS).
+template <int BS, int U>
+__device__ __forceinline__ void seq_extent(const DecodeParams& P, int b, int32_t* L_out, int32_t* lo_out,
+                                           int32_t* first_out, int32_t* nunits_out) {
+  extent_of<BS, U>(P, P.lens[b], L_out, lo_out, first_out, nunits_out);
+}
+
+// Exclusive prefix sums of the per-sequence unit counts into C[0..B] (LDS);
+// with lens_in_lds the context lengths follow, at C[B + 1 + b].
 template <int BS, int U>
 __device__ void scan_units(const DecodeParams& P, int32_t* C) {
   __shared__ int32_t part[256];
@@ -314,9 +323,11 @@ __device__ void scan_units(const DecodeParams& P, int32_t* C) {
   const int b1 = min(P.batch, b0 + per);
   int32_t local = 0;
   for (int b = b0; b < b1; ++b) {
+    const int32_t raw = P.lens[b];
     int32_t L, lo, first, nu;
-    seq_extent<BS, U>(P, b, &L, &lo, &first, &nu);
+    extent_of<BS, U>(P, raw, &L, &lo, &first, &nu);
     C[b] = nu;
+    if (P.lens_in_lds) C[P.batch + 1 + b] = raw;
     local += nu;
   }
   part[tid] = local;
@@ -735,7 +746,8 @@ struct Decoder {
                                                  int b) {
     Seg s;
     int32_t nu;
-    seq_extent<BS, U>(P, b, &s.L, &s.lo, &s.first, &nu);
+    const int32_t raw = C && P.lens_in_lds ? C[P.batch + 1 + b] : P.lens[b];
+    extent_of<BS, U>(P, raw, &s.L, &s.lo, &s.first, &nu);
     s.g = g;
     s.b = b;
     s.L = uniform(s.L);
@@ -1098,15 +1110,11 @@ struct Decoder {
     int32_t tcur = table_chunk(P, ls.b, tb0, tb1, 0, lane);
     int32_t tnext = tb1 - tb0 > 64 ? table_chunk(P, ls.b, tb0, tb1, 1, lane) : -1;
     int ccur = 0;
-    // the piece after it, with its first table entries in flight
+    // the piece after it, with its first table entries in flight (looked up
+    // once the first sub-tile's loads are out)
     Seg ln = ls;
-    bool has_ln = C && lend < r1 && next_seg(P, C, t_head, ls, ln);
+    bool has_ln = false;
     int32_t tpn = -1;
-    if (has_ln) {
-      int32_t nb0, nb1;
-      piece_blocks(ln, ln.start, min(r1, ln.start + ln.nb), &nb0, &nb1);
-      tpn = table_chunk(P, ln.b, nb0, nb1, 0, lane);
-    }
     qop q[NQ], qn[NQ];
     load_q(P, ls.b, ls.g, i, kg, q);
 
@@ -1192,31 +1200,42 @@ struct Decoder {
     Addr a1 = a0;
     load_k(K0, a0);
     load_v(V0, a0);
+    __builtin_amdgcn_sched_barrier(0);
+    has_ln = C && lend < r1 && next_seg(P, C, t_head, ls, ln);
+    if (has_ln) {
+      int32_t nb0, nb1;
+      piece_blocks(ln, ln.start, min(r1, ln.start + ln.nb), &nb0, &nb1);
+      tpn = table_chunk(P, ln.b, nb0, nb1, 0, lane);
+    }
     // sched_barrier keeps the compiler from hoisting the next sub-tile's
     // loads above the current one's math (that would hold three half-tiles
     // at once and spill).
     for (int64_t s = 0; s < nsub; s += 2) {
       const bool n1 = s + 1 < nsub;
-      if (n1) a1 = where(last1);
-      load_k(K1, a1);
+      if (n1) {
+        a1 = where(last1);
+        load_k(K1, a1);
+      }
       __builtin_amdgcn_sched_barrier(0);
       qk(K0, q, S);
       softmax(V0, S, st, p, cs.lo, cs.L, P.scale_log2, kg);
       __builtin_amdgcn_sched_barrier(0);
-      load_v(V1, a1);
+      if (n1) load_v(V1, a1);
       __builtin_amdgcn_sched_barrier(0);
       pv(V0, p, st, cs.lo, cs.L, kg);
       __builtin_amdgcn_sched_barrier(0);
       if (last0) step_piece(n1);
       if (!n1) break;
       const bool n2 = s + 2 < nsub;
-      if (n2) a0 = where(last0);
-      load_k(K0, a0);
+      if (n2) {
+        a0 = where(last0);
+        load_k(K0, a0);
+      }
       __builtin_amdgcn_sched_barrier(0);
       qk(K1, q, S);
       softmax(V1, S, st, p, cs.lo, cs.L, P.scale_log2, kg);
       __builtin_amdgcn_sched_barrier(0);
-      load_v(V0, a0);
+      if (n2) load_v(V0, a0);
       __builtin_amdgcn_sched_barrier(0);
       pv(V1, p, st, cs.lo, cs.L, kg);
       __builtin_amdgcn_sched_barrier(0);
@@ -1819,6 +1838,7 @@ static pkv_status decode_launch(const kv_pool* pool, const paged_decode_args* a,
   P.xcd_remap = 0;
   P.nstage = 0;
   P.stage_off = 0;
+  P.lens_in_lds = 0;
   P.shared = a->shared_prefix_blocks;
   P.pre_chunks = 0;
   P.pre_rtiles = 0;
@@ -1876,9 +1896,11 @@ static pkv_status decode_launch(const kv_pool* pool, const paged_decode_args* a,
   int64_t grid = (W + 3) / 4;
   grid = ((grid + 7) / 8) * 8;  // whole rounds over the 8 XCDs
   P.xcd_remap = 1;
-  // unit prefix sums, then as many staging slots per wavefront (at most 4)
-  // as fit, with the static LDS, in 64 KiB
-  P.stage_off = (int32_t)(((a->batch + 1) * (int64_t)sizeof(int32_t) + 15) / 16 * 16);
+  // unit prefix sums (and, up to 4096 sequences, the context lengths), then
+  // as many staging slots per wavefront (at most 4) as fit, with the static
+  // LDS, in 64 KiB
+  P.lens_in_lds = a->batch <= 4096 ? 1 : 0;
+  P.stage_off = (int32_t)(((a->batch + 1 + (P.lens_in_lds ? a->batch : 0)) * (int64_t)sizeof(int32_t) + 15) / 16 * 16);
   const int64_t per_slot = 4 * (int64_t)(4 * P.group * (d.head_dim + 8) + (int64_t)sizeof(PieceTag));
   P.nstage = (int32_t)std::max<int64_t>(0, std::min<int64_t>(4, (63488 - P.stage_off) / per_slot));
   const size_t lds = (size_t)P.stage_off + (size_t)P.nstage * per_slot;
