@@ -411,6 +411,25 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// wait_vmem<a * NG>() for a run-time a in [0, A] (a is wave-uniform).
+template <int NG, int A>
+__device__ __forceinline__ void wait_stages(int a) {
+  if constexpr (A > 0) {
+    if (a >= A) {
+      wait_vmem<A * NG>();
+      return;
+    }
+    wait_stages<NG, A - 1>(a);
+  } else {
+    wait_vmem<0>();
+  }
+}
+
+// LDS slots of the shared-prefix pipeline (16 KiB each)
+#ifndef PKV_PREFIX_STAGES
+#define PKV_PREFIX_STAGES 6
+#endif
+
 // 16 bytes as 8 x 16-bit MFMA operand elements
 template <typename V8>
 __device__ __forceinline__ V8 as8(const uint4& w) {
@@ -939,7 +958,7 @@ struct Decoder {
   static constexpr int VG = NV * 64;
   // LDS bytes of one staged sub-tile (three are used)
   static constexpr int STAGE_BYTES = (KG + VG) * 16;
-  static constexpr int STAGES = 3;
+  static constexpr int STAGES = PKV_PREFIX_STAGES;
 
   // Shared prefix, one workgroup of 4 wavefronts: query rows
   // rg*64*NT .. +64*NT of KV head g (wavefront wv takes 16*NT of them; row
@@ -1029,24 +1048,22 @@ struct Decoder {
     };
 
     if (s0 < s1) {
-      // three LDS slots: two sub-tiles in flight while one is used
-      issue(s0, 0);
-      if (s0 + 1 < s1) issue(s0 + 1, 1);
+      // STAGES LDS slots: STAGES - 1 sub-tiles in flight while one is used;
+      // sub-tile x lives in slot (x - s0) % STAGES
+      for (int k = 0; k < STAGES - 1 && s0 + k < s1; ++k) issue(s0 + k, k);
       KTile K;
       VTile V;
       f32x4 S[NQT];
       float pp[NT][NQT][4];
       int slot = 0;
       for (int32_t s = s0; s < s1; ++s) {
-        // slot (s + 2) % 3 was last read in iteration s - 1, before its
-        // closing barrier
-        const int ahead = (s + 2 < s1) ? 2 : (s + 1 < s1 ? 1 : 0);
-        if (ahead == 2) issue(s + 2, slot == 0 ? 2 : slot - 1);
+        // the slot of sub-tile s - 1 was last read in iteration s - 1,
+        // before its closing barrier
+        if (s + STAGES - 1 < s1) issue(s + STAGES - 1, slot == 0 ? STAGES - 1 : slot - 1);
         // sub-tile s has landed once no more than `ahead` stages (NG loads
         // each) are outstanding: this thread's, then every thread's
-        if (ahead == 2) wait_vmem<2 * NG>();
-        else if (ahead == 1) wait_vmem<NG>();
-        else wait_vmem<0>();
+        const int ahead = min(STAGES - 1, s1 - 1 - s);
+        wait_stages<NG, STAGES - 1>(ahead);
         __syncthreads();
         const uint4* src = reinterpret_cast<const uint4*>(lds + slot * STAGE_BYTES);
 #pragma unroll
@@ -1064,7 +1081,7 @@ struct Decoder {
 #pragma unroll
         for (int t = 0; t < NT; ++t) pv(V, pp[t], st[t], 0, kT, kg);
         __syncthreads();   // every wavefront is done with this slot
-        slot = slot == 2 ? 0 : slot + 1;
+        slot = slot == STAGES - 1 ? 0 : slot + 1;
       }
     }
 
@@ -1241,7 +1258,9 @@ struct Decoder {
       __builtin_amdgcn_sched_barrier(0);
       if (last1) step_piece(n2);
     }
-    // the staged pieces, now that no load is in flight
+    // the staged pieces, now that no load is in flight (their tags were
+    // written by lane 0 and are read by every lane: keep the reads below)
+    asm volatile("" ::: "memory");
     for (int k = 0; k < nst; ++k) {
       Seg ps;
       int64_t pbeg, pend;
