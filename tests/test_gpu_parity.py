@@ -293,6 +293,46 @@ def test_workspace_reused_across_calls():
             assert np.abs(got - ref[:B]).max() <= TOL[w.kv_dtype], (rep, s, B)
 
 
+def test_large_batch_lengths_read_from_memory():
+    # more than 4096 sequences: the decode keeps only the unit prefix sums in
+    # LDS and reads a sequence's length from memory when it starts a piece;
+    # short ragged lengths (some empty) give every range many pieces, more
+    # than its LDS staging slots hold
+    w = wl.scaled(wl.WORKLOADS["c3"], batch=4200, num_q_heads=8, num_kv_heads=2, lengths_kind="uniform",
+                  lengths_args=(0, 20))
+    d = wl.draw(w)
+    ost = OracleState(w, d)
+    gst = GpuState(w, d)
+    try:
+        tables, lens = ost.export()
+        assert (lens == 0).any() and w.batch > 4096
+        q = wl.q_bits(w)
+        ref = _oracle_out(ost, q, tables, lens)
+        for splits in (0, 3):
+            got = gst.decode(q, tables, lens, num_splits=splits)
+            assert np.abs(got - ref).max() <= TOL[w.kv_dtype], splits
+            assert not got[lens == 0].any(), splits
+    finally:
+        gst.close()
+
+
+def test_every_sequence_empty():
+    # nothing to attend anywhere: every output row is zero, in both modes
+    w = wl.scaled(wl.WORKLOADS["c3"], batch=5, num_q_heads=8, num_kv_heads=2, lengths_kind="fixed",
+                  lengths_args=(0, 0, 0, 0, 0), pool_blocks=4)
+    d = wl.draw(w)
+    gst = GpuState(w, d)
+    try:
+        tables = np.full((w.batch, 2), -1, dtype=np.int32)
+        lens = np.zeros(w.batch, dtype=np.int32)
+        q = wl.q_bits(w)
+        for splits in (1, 0, 4):
+            got = gst.decode(q, tables, lens, num_splits=splits)
+            assert np.array_equal(got, np.zeros_like(got)), splits
+    finally:
+        gst.close()
+
+
 @pytest.mark.parametrize("window", [16, 40, 100])
 def test_window_release_decodes_the_same(window):
     # releasing every block wholly before the window (block_table_release_before)
