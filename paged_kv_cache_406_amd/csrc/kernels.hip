@@ -425,9 +425,10 @@ __device__ __forceinline__ void wait_stages(int a) {
   }
 }
 
-// LDS slots of the shared-prefix pipeline (16 KiB each)
+// LDS slots of the shared-prefix pipeline (16 KiB each); two workgroups of
+// prefix_kernel share a CU
 #ifndef PKV_PREFIX_STAGES
-#define PKV_PREFIX_STAGES 6
+#define PKV_PREFIX_STAGES 3
 #endif
 
 // 16 bytes as 8 x 16-bit MFMA operand elements
@@ -1336,7 +1337,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // KV-head major, so the workgroups of one head sit on one XCD and its prefix
 // blocks stay in that XCD's L2.
 template <int KV, int D, int BS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefix_kernel(DecodeParams P) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefix_kernel(DecodeParams P) {
   typedef Decoder<KV, D, BS> Dec;
   __shared__ __attribute__((aligned(16))) uint8_t stage[Dec::STAGES * Dec::STAGE_BYTES];
   int64_t wg = blockIdx.x;
@@ -1558,7 +1559,8 @@ static void prefix_plan(const kv_pool* pool, const paged_decode_args* a, int cus
   const int64_t rt = ((int64_t)a->batch * G + rows_per_group - 1) / rows_per_group;
   const int64_t tt = tokens_per_subtile(d.kv_dtype);
   const int64_t nsp = ((int64_t)a->shared_prefix_blocks * d.block_size + tt - 1) / tt;
-  int64_t c = (int64_t)cus / std::max<int64_t>(1, d.num_kv_heads * rt);
+  // two workgroups per CU (two wavefronts per SIMD hide each other's waits)
+  int64_t c = 2 * (int64_t)cus / std::max<int64_t>(1, d.num_kv_heads * rt);
   c = std::max<int64_t>(1, std::min<int64_t>({c, nsp, 16}));
   *rtiles = (int32_t)rt;
   *chunks = (int32_t)c;
