@@ -1416,20 +1416,40 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams P) {
       M = Mb;
     }
     // the prefix partials of this (sequence, head), and (job.w) the partial
-    // of its own part when one wavefront held all of it: same fold
+    // of its own part when one wavefront held all of it: same fold, also up
+    // to NPC partials per thread per round trip
     if (P.shared) {
       const int64_t bhq = (int64_t)P.batch * P.hq;
       const int64_t hrow = (int64_t)b * P.hq + (int64_t)g * G + h;
       const int nslots = P.pre_chunks + (job.w ? 1 : 0);
-      for (int cc = sub; cc < nslots; cc += tpp) {
-        const float* base = P.ws_pre + ((int64_t)cc * bhq + hrow) * (D + 4);
-        const float mc = base[D];
-        const float Mb = fmaxf(M, mc);
+      for (int cb = sub; cb < nslots; cb += NPC * tpp) {
+        f32x2 ml[NPC];
+        f32x4 o[NPC];
+#pragma unroll
+        for (int k = 0; k < NPC; ++k) {
+          const int cc = cb + k * tpp;
+          if (cc < nslots) {
+            const float* base = P.ws_pre + ((int64_t)cc * bhq + hrow) * (D + 4);
+            ml[k] = *reinterpret_cast<const f32x2*>(base + D);
+            o[k] = *reinterpret_cast<const f32x4*>(base + d4);
+          } else {
+            ml[k] = f32x2{-INFINITY, 0.f};
+            o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+        }
+        float Mb = M;
+#pragma unroll
+        for (int k = 0; k < NPC; ++k) Mb = fmaxf(Mb, ml[k][0]);
         const float Mu = Mb == -INFINITY ? 0.f : Mb;
         const float r = __builtin_amdgcn_exp2f(M - Mu);
-        const float wt = __builtin_amdgcn_exp2f(mc - Mu);
-        acc = acc * r + *reinterpret_cast<const f32x4*>(base + d4) * wt;
-        Ls = Ls * r + base[D + 1] * wt;
+        acc *= r;
+        Ls *= r;
+#pragma unroll
+        for (int k = 0; k < NPC; ++k) {
+          const float wt = __builtin_amdgcn_exp2f(ml[k][0] - Mu);
+          acc += o[k] * wt;
+          Ls += ml[k][1] * wt;
+        }
         M = Mb;
       }
     }
