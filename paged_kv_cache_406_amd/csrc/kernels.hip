@@ -63,6 +63,7 @@
 namespace pkv {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
@@ -180,14 +181,19 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams P) {
   uint8_t* kdst = P.kc + ((tile * (P.d / X) + c) * P.bs + off) * 16;
   uint8_t* vdst = P.vc + (tile * P.d + (int64_t)c * X) * P.bs * EB + (int64_t)off * EB;
   if constexpr (KV == SRC) {
-    const uint4 kv = *reinterpret_cast<const uint4*>(P.k + src0 * EB);
-    *reinterpret_cast<uint4*>(kdst) = kv;
+    // non-temporal stores: the cache lines this token touches (one 16-byte
+    // K group, D two- or four-byte V elements each in its own line) are not
+    // read again by this kernel
+    const u32x4 kv = *reinterpret_cast<const u32x4*>(P.k + src0 * EB);
+    __builtin_nontemporal_store(kv, reinterpret_cast<u32x4*>(kdst));
     const uint8_t* vs = P.v + src0 * EB;
 #pragma unroll
     for (int e = 0; e < X; ++e) {
       uint8_t* dst = vdst + (int64_t)e * P.bs * EB;
-      if constexpr (EB == 4) *reinterpret_cast<uint32_t*>(dst) = reinterpret_cast<const uint32_t*>(vs)[e];
-      else if constexpr (EB == 2) *reinterpret_cast<uint16_t*>(dst) = reinterpret_cast<const uint16_t*>(vs)[e];
+      if constexpr (EB == 4)
+        __builtin_nontemporal_store(reinterpret_cast<const uint32_t*>(vs)[e], reinterpret_cast<uint32_t*>(dst));
+      else if constexpr (EB == 2)
+        __builtin_nontemporal_store(reinterpret_cast<const uint16_t*>(vs)[e], reinterpret_cast<uint16_t*>(dst));
     }
   } else {
     static_assert(KV == KV_FP8, "only same-dtype copy or FP8 quantisation");
@@ -198,9 +204,9 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams P) {
       const float kx = src_to_f32<SRC>(P.k, src0 + e) * P.k_inv[s0 + e];
       const float vx = src_to_f32<SRC>(P.v, src0 + e) * P.v_inv[s0 + e];
       kw[e >> 2] |= f32_to_e4m3(kx) << (8 * (e & 3));
-      vdst[(int64_t)e * P.bs] = (uint8_t)f32_to_e4m3(vx);
+      __builtin_nontemporal_store((uint8_t)f32_to_e4m3(vx), vdst + (int64_t)e * P.bs);
     }
-    *reinterpret_cast<uint4*>(kdst) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
+    __builtin_nontemporal_store(u32x4{kw[0], kw[1], kw[2], kw[3]}, reinterpret_cast<u32x4*>(kdst));
   }
 }
 
@@ -216,10 +222,13 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* kc, uint8_t* 
   const int32_t src = pairs[pair].src;
   const int32_t dst = pairs[pair].dst;
   if (src < 0 || dst < 0 || src >= num_blocks || dst >= num_blocks) return;
-  const uint4* s = reinterpret_cast<const uint4*>(base + ((int64_t)layer * num_blocks + src) * tile_bytes);
-  uint4* d = reinterpret_cast<uint4*>(base + ((int64_t)layer * num_blocks + dst) * tile_bytes);
+  const u32x4* s = reinterpret_cast<const u32x4*>(base + ((int64_t)layer * num_blocks + src) * tile_bytes);
+  u32x4* d = reinterpret_cast<u32x4*>(base + ((int64_t)layer * num_blocks + dst) * tile_bytes);
   const int64_t n16 = tile_bytes / 16;
-  for (int64_t i = threadIdx.x; i < n16; i += blockDim.x) d[i] = s[i];
+  // streamed: neither copy is read again by this kernel, and dirty lines
+  // left in L2 would be written back while the next kernel runs
+  for (int64_t i = threadIdx.x; i < n16; i += blockDim.x)
+    __builtin_nontemporal_store(__builtin_nontemporal_load(s + i), d + i);
 }
 
 // ---------------------------------------------------------------------------
@@ -386,7 +395,6 @@ __device__ __forceinline__ void write_zero_rows(const DecodeParams& P, int b, in
 
 // 16-byte streaming load: the cache is read once per call, so K/V tiles
 // are loaded non-temporally (no cache allocation for data that is not reused)
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 load_stream(const uint8_t* p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
