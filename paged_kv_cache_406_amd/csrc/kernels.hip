@@ -158,12 +158,23 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams P) {
   const int chunks = P.d / X;
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = (int64_t)P.n * P.hkv * chunks;
-  if (t >= total) return;
+  const int64_t per_row = (int64_t)chunks * P.hkv;
   const int c = (int)(t % chunks);
   const int h = (int)((t / chunks) % P.hkv);
-  const int64_t i = t / ((int64_t)chunks * P.hkv);
-  const int64_t slot = P.tables ? __hip_atomic_load(P.slots + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)
-                                : P.slots[i];
+  const int64_t i = t / per_row;
+  // The threads of one token are consecutive: the first lane of each token
+  // in the wavefront reads its slot (from page-locked host memory, one
+  // transfer per token rather than one per thread) and the others take it
+  // from that lane.  The source lane is never past the reading lane, so it
+  // is active whenever the reading lane is.
+  const int lane = (int)(threadIdx.x & 63);
+  const int64_t pos = t - i * per_row;
+  const int src = pos <= lane ? lane - (int)pos : 0;
+  int64_t slot = -1;
+  if (t < total && lane == src)
+    slot = P.tables ? __hip_atomic_load(P.slots + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) : P.slots[i];
+  slot = __shfl(slot, src);
+  if (t >= total) return;
   if (slot < 0 || slot >= P.num_blocks * P.bs) return;
   const int64_t blk = slot / P.bs;
   const int off = (int)(slot % P.bs);
@@ -177,34 +188,41 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams P) {
     }
   }
   const int64_t tile = ((int64_t)P.layer * P.num_blocks + blk) * P.hkv + h;
-  const int64_t src0 = (i * P.hkv + h) * P.d + (int64_t)c * X;  // element index
+  const int64_t row = (i * P.hkv + h) * P.d;       // element index of the token's (head) row
+  const int64_t src0 = row + (int64_t)c * X;       // this thread's K chunk
   uint8_t* kdst = P.kc + ((tile * (P.d / X) + c) * P.bs + off) * 16;
-  uint8_t* vdst = P.vc + (tile * P.d + (int64_t)c * X) * P.bs * EB + (int64_t)off * EB;
+  // V is channel-major: element dim of this token sits bs elements after
+  // element dim - 1.  The thread's e-th V element is dim e * chunks + c, so
+  // the lanes of one store instruction cover consecutive dims, and the dims
+  // that share a cache line are written by one instruction.
+  uint8_t* vdst = P.vc + (tile * P.d * P.bs + off) * EB;
   if constexpr (KV == SRC) {
     // non-temporal stores: the cache lines this token touches (one 16-byte
-    // K group, D two- or four-byte V elements each in its own line) are not
+    // K group, D two- or four-byte V elements in bs-element rows) are not
     // read again by this kernel
     const u32x4 kv = *reinterpret_cast<const u32x4*>(P.k + src0 * EB);
     __builtin_nontemporal_store(kv, reinterpret_cast<u32x4*>(kdst));
-    const uint8_t* vs = P.v + src0 * EB;
 #pragma unroll
     for (int e = 0; e < X; ++e) {
-      uint8_t* dst = vdst + (int64_t)e * P.bs * EB;
+      const int64_t dim = (int64_t)e * chunks + c;
+      uint8_t* dst = vdst + dim * P.bs * EB;
       if constexpr (EB == 4)
-        __builtin_nontemporal_store(reinterpret_cast<const uint32_t*>(vs)[e], reinterpret_cast<uint32_t*>(dst));
+        __builtin_nontemporal_store(reinterpret_cast<const uint32_t*>(P.v)[row + dim], reinterpret_cast<uint32_t*>(dst));
       else if constexpr (EB == 2)
-        __builtin_nontemporal_store(reinterpret_cast<const uint16_t*>(vs)[e], reinterpret_cast<uint16_t*>(dst));
+        __builtin_nontemporal_store(reinterpret_cast<const uint16_t*>(P.v)[row + dim], reinterpret_cast<uint16_t*>(dst));
     }
   } else {
     static_assert(KV == KV_FP8, "only same-dtype copy or FP8 quantisation");
-    const int64_t s0 = ((int64_t)P.layer * P.hkv + h) * P.d + (int64_t)c * X;
+    const int64_t s0 = ((int64_t)P.layer * P.hkv + h) * P.d;   // channel scales of (layer, head)
     uint32_t kw[4] = {0, 0, 0, 0};
 #pragma unroll
     for (int e = 0; e < X; ++e) {
-      const float kx = src_to_f32<SRC>(P.k, src0 + e) * P.k_inv[s0 + e];
-      const float vx = src_to_f32<SRC>(P.v, src0 + e) * P.v_inv[s0 + e];
+      const int kd = c * X + e;
+      const float kx = src_to_f32<SRC>(P.k, row + kd) * P.k_inv[s0 + kd];
       kw[e >> 2] |= f32_to_e4m3(kx) << (8 * (e & 3));
-      __builtin_nontemporal_store((uint8_t)f32_to_e4m3(vx), vdst + (int64_t)e * P.bs);
+      const int64_t vd = (int64_t)e * chunks + c;
+      const float vx = src_to_f32<SRC>(P.v, row + vd) * P.v_inv[s0 + vd];
+      __builtin_nontemporal_store((uint8_t)f32_to_e4m3(vx), vdst + vd * P.bs);
     }
     __builtin_nontemporal_store(u32x4{kw[0], kw[1], kw[2], kw[3]}, reinterpret_cast<u32x4*>(kdst));
   }
