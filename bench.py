@@ -305,7 +305,7 @@ def run(args):
     ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
     # pinned staging ring for the per-step metadata; a buffer is rewritten only
     # once the upload that last read it has run
-    RING = 8
+    RING = 16   # two sampling periods: the host waits on a step at least 8 behind
     ring = []
     for _ in range(RING):
         buf = torch.empty(reps[0].n_meta, dtype=torch.int32, pin_memory=True)
@@ -339,7 +339,7 @@ def run(args):
     # of steps carries them.  The last event of a sampled step also tells the
     # host that the kernels up to that step have finished reading the
     # page-locked staging buffers (staging ring reuse).
-    TIME_EVERY = 4
+    TIME_EVERY = 8
     sampled = {t: [HipEvent() for _ in range(4)]
                for t in sorted(set(range(0, n_total, TIME_EVERY)) | {args.warmup})}
     torch.cuda.synchronize()
@@ -642,7 +642,7 @@ def copy_probe(nbytes, reps):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c3", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--splits", type=int, default=0, help="num_splits passed to decode (0 = automatic)")

@@ -617,9 +617,17 @@ struct Decoder {
         T.k[t * NKJ + j] = load_stream(a.krow + (4 * j * BS + 4 * t) * 16);
   }
 
+  // A V row (one channel of a block) is BS * EB bytes.  When a sub-tile
+  // covers less than a 128-byte line of it (BS > TT and TT * EB < 128: bf16
+  // and fp16 at BS >= 64, fp32 at BS >= 32, FP8 at BS = 128), the next
+  // sub-tile of the same block reads the rest of that line: those loads keep
+  // the line in L2 instead of streaming past it.
+  static constexpr bool V_PART_LINE = BS > TT && TT * EB < 128;
   static __device__ __forceinline__ void load_v(VTile& T, const Addr& a) {
 #pragma unroll
-    for (int n = 0; n < NV; ++n) T.v[n] = load_stream(a.vrow + 16 * n * BS * EB);
+    for (int n = 0; n < NV; ++n)
+      T.v[n] = V_PART_LINE ? *reinterpret_cast<const uint4*>(a.vrow + 16 * n * BS * EB)
+                           : load_stream(a.vrow + 16 * n * BS * EB);
     T.tok0 = a.tok0;
     T.ok = a.ok;
   }
