@@ -626,6 +626,26 @@ def cpu_baseline(w, d, budget_s, scales=None):
     }
 
 
+def read_probe(nbytes, reps):
+    """Achievable HBM read rate on this device: pkv_hbm_read_probe over a
+    buffer of nbytes (several times the 256 MB Infinity Cache), timed with
+    events around each call on one stream; the median in GB/s."""
+    import torch
+    buf = torch.full((nbytes // 4,), 1.0, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    s = torch.cuda.current_stream()
+    P.pkv_hbm_read_probe(buf, nbytes, sink, stream=s.cuda_stream)   # warm-up
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record(s)
+        P.pkv_hbm_read_probe(buf, nbytes, sink, stream=s.cuda_stream)
+        b.record(s)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+    del buf
+    return nbytes / (ms * 1e-3) / 1e9
+
+
 def copy_probe(nbytes, reps):
     """A plain device-to-device copy of known size, run under rocprofv3 --pmc
     so that FETCH_SIZE / WRITE_SIZE can be calibrated against bytes moved."""
@@ -657,15 +677,24 @@ def main():
                     help="HBM bytes per decode_kernel launch from rocprofv3 counters (GB)")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
+    ap.add_argument("--read-probe", type=int, default=0,
+                    help="only run the streaming HBM read probe over this many bytes")
     args = ap.parse_args()
     if args.copy_probe:
         copy_probe(args.copy_probe, 5)
+        return
+    if args.read_probe:
+        print(json.dumps({"read_probe_bytes": args.read_probe,
+                          "GBps": round(read_probe(args.read_probe, 20), 1)}), flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the decode path runs on a single MI355X; "
               "multi-GPU runs are not part of this benchmark", file=sys.stderr)
         sys.exit(2)
     res, w, d, scales = run(args)
+    # context for the roofline: what a plain streaming read of 2 GiB reaches
+    # on this device (pkv_hbm_read_probe, median of 10 calls)
+    res["hbm_read_probe_GBps"] = round(read_probe(1 << 31, 10), 1)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(w, d, args.cpu_budget, scales)

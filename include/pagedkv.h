@@ -387,6 +387,18 @@ pkv_status paged_attention_decode_timed(const kv_pool* pool, const paged_decode_
                                         pkv_stream stream, void* const* kernel_events,
                                         int32_t* n_kernels_out);
 
+/* Measurement helper, not part of the method: reads [d_buf, d_buf + bytes)
+ * of device memory once, with the 16-byte streaming loads the decode uses for
+ * K and V, so that the time of this call is the achievable HBM read rate that
+ * the decode's own rate can be compared with (the decode is bound by HBM
+ * bandwidth: page "生成一个字…", section "显存账本", every generated token
+ * reads the whole KV cache).  d_buf: device, 16-byte aligned, bytes a
+ * multiple of 16, inside one allocation; d_sink: device, 4 bytes, written
+ * only when the XOR of what one thread read equals tag.  Asynchronous on
+ * stream.  PKV_E_INVAL on a bad pointer or size. */
+pkv_status pkv_hbm_read_probe(const void* d_buf, size_t bytes, uint32_t* d_sink, uint32_t tag,
+                              pkv_stream stream);
+
 /* Message describing the last failure on the calling thread ("" if none). */
 const char* pkv_last_error(void);
 

@@ -97,6 +97,7 @@ _SIGS = {
     "prefix_cache_stats": (c_i32, [c_vp, P_i32, P_i32]),
     "kv_pool_copy_blocks": (c_i32, [P_pool, c_vp, c_i32, c_vp]),
     "kv_metadata_upload": (c_i32, [c_vp, c_vp, c_size, c_vp]),
+    "pkv_hbm_read_probe": (c_i32, [c_vp, c_size, c_vp, ctypes.c_uint32, c_vp]),
     "paged_kv_append": (c_i32, [P_pool, c_i32, c_vp, c_vp, c_i32, c_vp, c_i32, c_vp]),
     "paged_kv_append_step": (c_i32, [P_pool, c_i32, c_vp, c_vp, c_i32, c_vp, c_i32, c_vp, c_vp, c_i32, c_vp]),
     "paged_attention_workspace_size": (c_i32, [P_pool, ctypes.POINTER(paged_decode_args), ctypes.POINTER(c_size)]),
@@ -350,6 +351,12 @@ def kv_metadata_upload(d_dst, h_src, nbytes, stream=None) -> None:
     """Copy nbytes from page-locked host memory (a pinned tensor or address) to
     device memory with a kernel on the stream."""
     _check(_lib.kv_metadata_upload(_ptr(d_dst), _ptr(h_src), nbytes, _stream(stream)))
+
+
+def pkv_hbm_read_probe(d_buf, nbytes, d_sink, tag=0x9E3779B9, stream=None) -> None:
+    """Read nbytes of device memory once with the decode's streaming loads
+    (measurement helper: the achievable HBM read rate)."""
+    _check(_lib.pkv_hbm_read_probe(_ptr(d_buf), nbytes, _ptr(d_sink), tag, _stream(stream)))
 
 
 def paged_kv_append(pool, layer, d_k, d_v, src_dtype, d_slots, n_tokens, stream=None) -> None:

@@ -1506,6 +1506,34 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams P) {
 }
 
 // ---------------------------------------------------------------------------
+// HBM read probe (measurement only): the buffer read once with the 16-byte
+// streaming loads the decode uses for K and V.  Workgroup x reads one
+// contiguous chunk, four loads in flight per thread per round; the XOR of
+// what a thread read is stored only if it equals `tag`, so that the loads
+// cannot be dropped.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void read_probe_kernel(const u32x4* __restrict__ p, int64_t n16,
+                                                         uint32_t* __restrict__ sink, uint32_t tag) {
+  const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const int64_t beg = (int64_t)blockIdx.x * per;
+  const int64_t end = beg + per < n16 ? beg + per : n16;
+  uint32_t acc = 0;
+  int64_t x = beg + threadIdx.x;
+  for (; x + 3 * 256 < end; x += 4 * 256) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(p + x + u * 256);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; x < end; x += 256) {
+    const u32x4 v = __builtin_nontemporal_load(p + x);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == tag) sink[0] = acc;
+}
+
+// ---------------------------------------------------------------------------
 // metadata upload: page-locked host memory -> device memory, by a kernel
 // ---------------------------------------------------------------------------
 // A copy engine would need a hand-off between two hardware queues before and
@@ -1738,6 +1766,28 @@ static bool in_one_allocation(const void* p, size_t bytes, hipMemoryType kind) {
   }
   const uintptr_t b = reinterpret_cast<uintptr_t>(base), q = reinterpret_cast<uintptr_t>(p);
   return q >= b && bytes <= size && q - b <= size - bytes;
+}
+
+pkv_status pkv_hbm_read_probe(const void* d_buf, size_t bytes, uint32_t* d_sink, uint32_t tag,
+                              pkv_stream stream) {
+  if (bytes == 0) return PKV_OK;
+  if (!d_buf || !d_sink) return fail(PKV_E_INVAL, "null pointer");
+  if (reinterpret_cast<uintptr_t>(d_buf) % 16 || bytes % 16)
+    return fail(PKV_E_INVAL, "buffer must be 16-byte aligned and bytes a multiple of 16");
+  if (!in_one_allocation(d_buf, bytes, hipMemoryTypeDevice))
+    return fail(PKV_E_INVAL, "buffer is not inside one device allocation");
+  if (!in_one_allocation(d_sink, sizeof(uint32_t), hipMemoryTypeDevice))
+    return fail(PKV_E_INVAL, "sink is not inside one device allocation");
+  int cus = 0;
+  pkv_status st = device_cus(&cus);
+  if (st != PKV_OK) return st;
+  const int64_t n16 = (int64_t)(bytes / 16);
+  // 8 workgroups per CU, none with less than one round of loads
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(8 * (int64_t)cus, n16 / 1024));
+  hipLaunchKernelGGL(read_probe_kernel, dim3((uint32_t)blocks), dim3(256), 0, (hipStream_t)stream,
+                     static_cast<const u32x4*>(d_buf), n16, d_sink, tag);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? PKV_OK : hip_fail(e, "read probe launch");
 }
 
 pkv_status kv_metadata_upload(void* d_dst, const void* h_src, size_t bytes, pkv_stream stream) {
