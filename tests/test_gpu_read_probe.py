@@ -46,6 +46,8 @@ def test_read_probe_argument_checks():
     with pytest.raises(RuntimeError):
         P.pkv_hbm_read_probe(buf, 1000, sink)                     # not a multiple of 16
     with pytest.raises(RuntimeError):
-        P.pkv_hbm_read_probe(buf, 8192, sink)                     # past the allocation
+        # past the allocation (torch's caching allocator serves this tensor
+        # from a 2 MiB segment: 64 MiB reaches beyond it)
+        P.pkv_hbm_read_probe(buf, 64 << 20, sink)
     with pytest.raises(RuntimeError):
         P.pkv_hbm_read_probe(host, 1024, sink)                    # host memory
