@@ -631,6 +631,7 @@ def read_probe(nbytes, reps):
     buffer of nbytes (several times the 256 MB Infinity Cache), timed with
     events around each call on one stream; the median in GB/s."""
     import torch
+    import paged_kv_cache_406_amd as P
     buf = torch.full((nbytes // 4,), 1.0, dtype=torch.float32, device="cuda")
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     s = torch.cuda.current_stream()
