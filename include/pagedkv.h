@@ -40,13 +40,15 @@
  *
  * Device memory layout of one pool (both buffers contiguous, caller-owned):
  *    x = 16 / bytes_per_element   (4 for fp32, 8 for fp16/bf16, 16 for fp8)
+ *    v = min(block_size, t), t = 16 for fp32, 32 for fp16/bf16, 64 for fp8
  *    K: [num_layers][num_blocks][num_kv_heads][head_dim / x][block_size][x]
- *    V: [num_layers][num_blocks][num_kv_heads][head_dim][block_size]
+ *    V: [num_layers][num_blocks][num_kv_heads][block_size / v][head_dim][v]
  *  Token `slot` of a block-table lives in physical block slot / block_size at
  *  offset slot % block_size.  Each (block, KV head) tile of K and of V is one
  *  contiguous run of block_size * head_dim elements.  K keeps 16-byte groups
- *  of channels of consecutive tokens together; V is stored channel-major
- *  inside the tile.
+ *  of channels of consecutive tokens together; V is stored channel-major in
+ *  runs of v tokens (the tokens the decode reads at a time), which is plain
+ *  channel-major [head_dim][block_size] when block_size <= t.
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H

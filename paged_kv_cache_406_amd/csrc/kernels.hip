@@ -130,6 +130,21 @@ template <> __device__ __forceinline__ float src_to_f32<KV_BF16>(const uint8_t* 
   return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p)[idx]);
 }
 
+// Tokens per sub-tile: the amount one wavefront loads and scores at a time.
+// Each lane group (16 lanes) holds TT/4 consecutive tokens of V, which is
+// 16 bytes for every element size.
+template <int KV> struct SubTile;
+template <> struct SubTile<KV_F32> { static constexpr int TT = 16; };
+template <> struct SubTile<KV_F16> { static constexpr int TT = 32; };
+template <> struct SubTile<KV_BF16> { static constexpr int TT = 32; };
+template <> struct SubTile<KV_FP8> { static constexpr int TT = 64; };
+
+// V inside a (block, KV head) tile: runs of VT = min(block size, TT)
+// tokens, channel-major within a run, [bs / VT][D][VT].  At bs <= TT that is
+// plain channel-major [D][bs]; for longer blocks each sub-tile's V is one
+// contiguous D * TT run.
+__host__ __device__ constexpr int v_run(int bs, int tt) { return bs < tt ? bs : tt; }
+
 // ---------------------------------------------------------------------------
 // append: tokens [n][Hkv][D] -> pool slots
 // ---------------------------------------------------------------------------
@@ -191,11 +206,13 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams P) {
   const int64_t row = (i * P.hkv + h) * P.d;       // element index of the token's (head) row
   const int64_t src0 = row + (int64_t)c * X;       // this thread's K chunk
   uint8_t* kdst = P.kc + ((tile * (P.d / X) + c) * P.bs + off) * 16;
-  // V is channel-major: element dim of this token sits bs elements after
-  // element dim - 1.  The thread's e-th V element is dim e * chunks + c, so
-  // the lanes of one store instruction cover consecutive dims, and the dims
-  // that share a cache line are written by one instruction.
-  uint8_t* vdst = P.vc + (tile * P.d * P.bs + off) * EB;
+  // V runs of vt tokens, channel-major inside a run: element dim of this
+  // token sits vt elements after element dim - 1.  The thread's e-th V
+  // element is dim e * chunks + c, so the lanes of one store instruction
+  // cover consecutive dims, and the dims that share a cache line are written
+  // by one instruction.
+  const int vt = v_run(P.bs, SubTile<KV>::TT);
+  uint8_t* vdst = P.vc + (tile * P.d * P.bs + (int64_t)(off / vt) * P.d * vt + off % vt) * EB;
   if constexpr (KV == SRC) {
     // non-temporal stores: the cache lines this token touches (one 16-byte
     // K group, D two- or four-byte V elements in bs-element rows) are not
@@ -205,7 +222,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams P) {
 #pragma unroll
     for (int e = 0; e < X; ++e) {
       const int64_t dim = (int64_t)e * chunks + c;
-      uint8_t* dst = vdst + dim * P.bs * EB;
+      uint8_t* dst = vdst + dim * vt * EB;
       if constexpr (EB == 4)
         __builtin_nontemporal_store(reinterpret_cast<const uint32_t*>(P.v)[row + dim], reinterpret_cast<uint32_t*>(dst));
       else if constexpr (EB == 2)
@@ -222,7 +239,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams P) {
       kw[e >> 2] |= f32_to_e4m3(kx) << (8 * (e & 3));
       const int64_t vd = (int64_t)e * chunks + c;
       const float vx = src_to_f32<SRC>(P.v, row + vd) * P.v_inv[s0 + vd];
-      __builtin_nontemporal_store((uint8_t)f32_to_e4m3(vx), vdst + vd * P.bs);
+      __builtin_nontemporal_store((uint8_t)f32_to_e4m3(vx), vdst + vd * vt);
     }
     __builtin_nontemporal_store(u32x4{kw[0], kw[1], kw[2], kw[3]}, reinterpret_cast<u32x4*>(kdst));
   }
@@ -300,14 +317,6 @@ struct PieceTag {
 };
 static_assert(sizeof(PieceTag) == 48, "staging tag layout");
 
-// Tokens per sub-tile: the amount one wavefront loads and scores at a time.
-// Each lane group (16 lanes) holds TT/4 consecutive tokens of V, which is
-// 16 bytes for every element size.
-template <int KV> struct SubTile;
-template <> struct SubTile<KV_F32> { static constexpr int TT = 16; };
-template <> struct SubTile<KV_F16> { static constexpr int TT = 32; };
-template <> struct SubTile<KV_BF16> { static constexpr int TT = 32; };
-template <> struct SubTile<KV_FP8> { static constexpr int TT = 64; };
 
 template <int KV, int BS>
 struct Units {
@@ -503,6 +512,7 @@ struct Decoder {
   static constexpr int NQ = KV == KV_F32 ? D / 4 : D / 32;  // q operands per lane
   static constexpr int EPW = 4 / EB;               // V elements per dword
   static constexpr int64_t TILE_BYTES = (int64_t)D * BS * EB;  // one (block, KV head) tile
+  static constexpr int VT = v_run(BS, TT);         // tokens per V run of a tile
 
   typedef typename std::conditional<KV == KV_F32, float,
           typename std::conditional<KV == KV_F16, f16x8, bf16x8>::type>::type qop;
@@ -601,7 +611,9 @@ struct Decoder {
     const bool okv = pv >= 0 && pv < P.num_blocks;
     const int64_t head_tile = (int64_t)P.layer * P.num_blocks * P.hkv + g;
     a.krow = P.kc + (head_tile + (int64_t)(okk ? pk : 0) * P.hkv) * TILE_BYTES + (uint32_t)(kg * BS + koff) * 16u;
-    a.vrow = P.vc + (head_tile + (int64_t)(okv ? pv : 0) * P.hkv) * TILE_BYTES + (uint32_t)(i * BS + voff) * (uint32_t)EB;
+    // V: run voff / VT of the tile, channel i, token voff % VT of the run
+    a.vrow = P.vc + (head_tile + (int64_t)(okv ? pv : 0) * P.hkv) * TILE_BYTES +
+             (uint32_t)(((voff / VT) * D + i) * VT + voff % VT) * (uint32_t)EB;
     a.tok0 = tok0;
     a.ok = okv;
     return a;
@@ -617,17 +629,12 @@ struct Decoder {
         T.k[t * NKJ + j] = load_stream(a.krow + (4 * j * BS + 4 * t) * 16);
   }
 
-  // A V row (one channel of a block) is BS * EB bytes.  When a sub-tile
-  // covers less than a 128-byte line of it (BS > TT and TT * EB < 128: bf16
-  // and fp16 at BS >= 64, fp32 at BS >= 32, FP8 at BS = 128), the next
-  // sub-tile of the same block reads the rest of that line: those loads keep
-  // the line in L2 instead of streaming past it.
-  static constexpr bool V_PART_LINE = BS > TT && TT * EB < 128;
+  // Channel 16n + i of the run: VT elements after channel 16n + i - 1.  A
+  // sub-tile's V is whole 128-byte lines (one run, or whole blocks), read
+  // once: streamed.
   static __device__ __forceinline__ void load_v(VTile& T, const Addr& a) {
 #pragma unroll
-    for (int n = 0; n < NV; ++n)
-      T.v[n] = V_PART_LINE ? *reinterpret_cast<const uint4*>(a.vrow + 16 * n * BS * EB)
-                           : load_stream(a.vrow + 16 * n * BS * EB);
+    for (int n = 0; n < NV; ++n) T.v[n] = load_stream(a.vrow + 16 * n * VT * EB);
     T.tok0 = a.tok0;
     T.ok = a.ok;
   }
@@ -1076,7 +1083,7 @@ struct Decoder {
           const int m = x0 >> 6;            // QK tile m / NKJ, step m % NKJ
           src = a.krow + (4 * (m % NKJ) * BS + 4 * (m / NKJ)) * 16;
         } else {
-          src = a.vrow + 16 * ((x0 - KG) >> 6) * BS * EB;
+          src = a.vrow + 16 * ((x0 - KG) >> 6) * VT * EB;
         }
         lds_dma16(src, lds0 + (uint32_t)(slot * STAGE_BYTES + x0 * 16));
       }

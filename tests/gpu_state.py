@@ -108,7 +108,10 @@ class GpuState:
         L, NB, H, BS, D = w.num_layers, self.d.num_blocks, w.num_kv_heads, w.block_size, w.head_dim
         k = from_dev(self.pool.k_cache, npd).reshape(L, NB, H, D // x, BS, x)
         k = k.transpose(0, 1, 2, 4, 3, 5).reshape(L, NB, H, BS, D)
-        v = from_dev(self.pool.v_cache, npd).reshape(L, NB, H, D, BS).transpose(0, 1, 2, 4, 3)
+        # V: runs of vt = min(bs, sub-tile tokens) tokens, channel-major in a run
+        vt = min(BS, {"f32": 16, "f16": 32, "bf16": 32, "fp8": 64}[w.kv_dtype])
+        v = from_dev(self.pool.v_cache, npd).reshape(L, NB, H, BS // vt, D, vt)
+        v = v.transpose(0, 1, 2, 3, 5, 4).reshape(L, NB, H, BS, D)
         return np.ascontiguousarray(k), np.ascontiguousarray(v)
 
     def close(self):

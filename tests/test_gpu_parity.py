@@ -42,6 +42,13 @@ CASES = {
     "gqa8_fp8_d64_bs32": wl.scaled(wl.WORKLOADS["c5_fp8"], batch=3, num_q_heads=8, num_kv_heads=1,
                                    head_dim=64, block_size=32, lengths_kind="fixed",
                                    lengths_args=(300, 33, 64), pool_blocks=0),
+    # blocks longer than a sub-tile: V tiles made of several runs
+    "f32_bs32": wl.scaled(C1, block_size=32, lengths_args=(5, 32, 33, 150), pool_blocks=0),
+    "f32_d128_bs128": wl.scaled(C1, head_dim=128, block_size=128, lengths_args=(5, 128, 129, 300),
+                                pool_blocks=0),
+    "gqa8_fp8_bs128": wl.scaled(wl.WORKLOADS["c5_fp8"], batch=3, num_q_heads=16, num_kv_heads=2,
+                                block_size=128, lengths_kind="fixed", lengths_args=(700, 129, 64),
+                                pool_blocks=0),
 }
 SPLITS = [1, 0, 2, 5, 64]
 _STATES = {}
