@@ -294,7 +294,11 @@ pkv_status block_table_append_batch(kv_pool* p, const int32_t* seqs, int32_t n,
   p->touched.clear();
   if (need < 0) return fail(PKV_E_INVAL, "sequence too long");
   if (need > p->count) return fail(PKV_E_OOM, "not enough free blocks");
-  for (int32_t i = 0; i < n; ++i) reserve_more(p->batch[i]->table, 1);
+  // only a sequence at a block boundary pushes a table entry (a copy-on-write
+  // replaces the last one): reserve for those, so that a fresh fork (table
+  // capacity == size) is not reallocated for nothing
+  for (int32_t i = 0; i < n; ++i)
+    if (p->batch[i]->len % bs == 0) reserve_more(p->batch[i]->table, 1);
   *n_cow_out = 0;
   for (int32_t i = 0; i < n; ++i) do_append(p, *p->batch[i], 1, slots_out + i, cow_out, n_cow_out);
   return PKV_OK;
@@ -427,13 +431,17 @@ pkv_status block_table_common_prefix(const kv_pool* p, const int32_t* seqs, int3
   int64_t k = 0;
   if (n > 0) {
     const Sequence& s0 = *p->batch[0];
-    k = (int64_t)s0.table.size();
-    for (int32_t i = 0; i < n; ++i) {
+    // row 0's leading valid entries
+    k = 0;
+    while (k < (int64_t)s0.table.size() && s0.table[k] >= 0) ++k;
+    for (int32_t i = 0; i < n && k > 0; ++i) {
       const Sequence& s = *p->batch[i];
       k = std::min<int64_t>(k, s.len / p->desc.block_size);   // full blocks only
       k = std::min<int64_t>(k, (int64_t)s.table.size());
+      // whole common run equal (the usual case for forks): one memcmp
+      if (k > 0 && std::memcmp(s.table.data(), s0.table.data(), (size_t)k * sizeof(int32_t)) == 0) continue;
       int64_t j = 0;
-      while (j < k && s.table[j] == s0.table[j] && s0.table[j] >= 0) ++j;
+      while (j < k && s.table[j] == s0.table[j]) ++j;
       k = j;
     }
   }
