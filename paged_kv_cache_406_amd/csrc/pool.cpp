@@ -70,6 +70,12 @@ static inline void reserve_more(std::vector<int32_t>& t, int64_t more) {
   if (t.capacity() < want) t.reserve(std::max<size_t>({want, 2 * t.capacity(), 16}));
 }
 
+// Freed sequences whose map nodes are kept for reuse by forks, and the
+// largest table (entries) a kept node may hold on to: at most 4 MiB of host
+// memory stays with the pool this way.
+static constexpr size_t kSpareNodes = 1024;
+static constexpr size_t kSpareTableCap = 1024;
+
 // Resolves a batch of sequence ids into p->batch, rejecting unknown and
 // repeated ids.
 static pkv_status resolve_batch(kv_pool* p, const int32_t* seqs, int32_t n) {
@@ -83,6 +89,19 @@ static pkv_status resolve_batch(kv_pool* p, const int32_t* seqs, int32_t n) {
     p->batch[i] = &it->second;
   }
   return PKV_OK;
+}
+
+// Freed sequence: its node goes to the spare list while there is room
+// (reserved, so this never allocates), else it is released.
+static void retire_sequence(kv_pool* p, int32_t id) {
+  auto nh = p->seqs.extract(id);
+  if (nh.empty() || p->spare.size() >= p->spare.capacity()) return;
+  Sequence& s = nh.mapped();
+  if (s.table.capacity() > kSpareTableCap) std::vector<int32_t>().swap(s.table);
+  s.table.clear();
+  s.len = 0;
+  s.mark = 0;
+  p->spare.push_back(std::move(nh));
 }
 
 // Performs an append whose block needs were checked; cannot fail.
@@ -178,6 +197,7 @@ pkv_status kv_pool_create(const kv_pool_desc* d, kv_pool** out) {
   const int32_t nb = d->num_blocks;
   p->ring.resize(nb);
   p->refcount.assign(nb, 0);
+  p->spare.reserve(kSpareNodes);
   if (d->free_order) {
     std::vector<char> seen(nb, 0);
     for (int32_t i = 0; i < nb; ++i) {
@@ -332,7 +352,7 @@ pkv_status block_table_free(kv_pool* p, int32_t seq) {
     p->refcount[b] -= 1;
     if (p->refcount[b] == 0) push_free(p, b);
   }
-  p->seqs.erase(it);
+  retire_sequence(p, seq);
   return PKV_OK;
   PKV_GUARD_END
 }
@@ -361,25 +381,48 @@ pkv_status block_table_fork_batch(kv_pool* p, const int32_t* parents, int32_t n,
   PKV_GUARD_BEGIN
   if (!p || n < 0 || (n > 0 && (!parents || !children_out))) return fail(PKV_E_INVAL, "bad argument");
   if ((int64_t)p->next_id + n > (int64_t)INT32_MAX) return fail(PKV_E_INVAL, "sequence ids exhausted");
-  // copy every parent first (may throw: nothing changed yet)
-  std::vector<Sequence> copies;
-  copies.reserve(n);
+  std::vector<const Sequence*> par(n);
   for (int32_t i = 0; i < n; ++i) {
     auto it = p->seqs.find(parents[i]);
     if (it == p->seqs.end()) return fail(PKV_E_INVAL, "unknown sequence id in batch");
-    copies.push_back(it->second);
+    par[i] = &it->second;
   }
+  // every child's node and table first, from the spare nodes where there are
+  // any (a failure here leaves the pool as it was: nodes not inserted are
+  // released, or go back to the spare list)
   const int32_t id0 = p->next_id;
-  int32_t done = 0;
+  std::vector<decltype(p->spare)::value_type> nodes;
+  nodes.reserve(n);
   try {
+    for (int32_t i = 0; i < n; ++i) {
+      decltype(p->spare)::value_type nh;
+      if (!p->spare.empty()) {
+        nh = std::move(p->spare.back());
+        p->spare.pop_back();
+      } else {
+        decltype(p->seqs) one;
+        one.emplace(0, Sequence());
+        nh = one.extract(one.begin());
+      }
+      nodes.push_back(std::move(nh));   // within the reserved room
+      Sequence& c = nodes.back().mapped();
+      nodes.back().key() = id0 + i;
+      c.table.assign(par[i]->table.begin(), par[i]->table.end());
+      c.len = par[i]->len;
+      c.mark = 0;
+    }
     p->seqs.reserve(p->seqs.size() + n);
-    for (; done < n; ++done) p->seqs.emplace(id0 + done, std::move(copies[done]));
   } catch (...) {
-    for (int32_t i = 0; i < done; ++i) p->seqs.erase(id0 + i);
+    while (!nodes.empty() && p->spare.size() < p->spare.capacity()) {
+      p->spare.push_back(std::move(nodes.back()));
+      nodes.pop_back();
+    }
     throw;
   }
+  // no allocation from here: the nodes exist and the buckets are reserved
   for (int32_t i = 0; i < n; ++i) {
-    for (int32_t b : p->seqs.find(id0 + i)->second.table)
+    auto res = p->seqs.insert(std::move(nodes[i]));
+    for (int32_t b : res.position->second.table)
       if (b >= 0) p->refcount[b] += 1;
     children_out[i] = id0 + i;
   }
@@ -400,7 +443,7 @@ pkv_status block_table_free_batch(kv_pool* p, const int32_t* seqs, int32_t n) {
       if (p->refcount[b] == 0) push_free(p, b);
     }
   }
-  for (int32_t i = 0; i < n; ++i) p->seqs.erase(seqs[i]);
+  for (int32_t i = 0; i < n; ++i) retire_sequence(p, seqs[i]);
   return PKV_OK;
   PKV_GUARD_END
 }

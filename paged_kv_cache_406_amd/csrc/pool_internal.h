@@ -27,6 +27,10 @@ struct kv_pool {
   int64_t count = 0;
   std::vector<int32_t> refcount;
   std::unordered_map<int32_t, pkv::Sequence> seqs;
+  // map nodes of freed sequences, tables cleared but still allocated, reused
+  // by forks: a steady fork/free loop allocates nothing (capacity fixed at
+  // creation, so keeping a node never allocates)
+  std::vector<std::unordered_map<int32_t, pkv::Sequence>::node_type> spare;
   int32_t next_id = 0;
   // scratch of the batch calls, kept between calls so that a steady decode
   // loop allocates nothing on the host
