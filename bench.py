@@ -629,7 +629,22 @@ def cpu_baseline(w, d, budget_s, scales=None):
                   f"attention)",
         "seq_heads_per_s": round(n * w.num_q_heads / elapsed, 2),
         "host_cpus": len(os.sched_getaffinity(0)),
+        "host_cpu_count": os.cpu_count(),
+        "cpu_model": _cpu_model(),
+        "blas": [f"{i.get('internal_api', '?')} {i.get('num_threads', '?')} threads" for i in info],
     }
+
+
+def _cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def read_probe(nbytes, reps):
