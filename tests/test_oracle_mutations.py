@@ -12,9 +12,11 @@ import oracle
 import oracle.allocator as alloc_mod
 import oracle.attention as att_mod
 import oracle.e4m3 as e4m3_mod
+import oracle.pool as pool_mod
 import test_oracle_allocator as TA
 import test_oracle_attention as TT
 import test_oracle_e4m3 as TE
+import test_oracle_pool as TP
 
 
 def _fails(fn, *args):
@@ -174,3 +176,50 @@ def test_release_without_freeing_is_caught(monkeypatch):
     pins = [lambda s=s: TA.test_random_ops_tiny_pools(s) for s in range(20)] + \
            [TA.test_window_release_bounds_held_blocks]
     assert _any_fails(pins)
+
+
+def _fp8_pool_pins():
+    return [lambda s=s: TP.test_fp8_append_codes_match_torch_cast(s) for s in ("bf16", "f16", "f32")] + \
+           [TP.test_fp8_append_special_values, TP.test_fp8_append_rounds_the_fp32_product_once]
+
+
+def test_pool_fp8_round_toward_zero_is_caught(monkeypatch):
+    orig = e4m3_mod.e4m3_encode
+
+    def rtz(x):
+        # truncate the magnitude to the code at or below it
+        a = np.asarray(x, dtype=np.float64)
+        c = orig(a)
+        t = e4m3_mod._TABLE
+        over = np.isfinite(a) & (np.abs(t[c]) > np.abs(a)) & ((c & 0x7F) != 0)
+        return np.where(over, c - 1, c).astype(np.uint8)
+    monkeypatch.setattr(pool_mod, "e4m3_encode", rtz)
+    assert _any_fails(_fp8_pool_pins())
+
+
+def test_pool_fp8_fp64_multiply_is_caught(monkeypatch):
+    def encode64(self, bits, src_dtype, inv_scale_layer):
+        if self.kv_dtype == src_dtype:
+            return np.asarray(bits, dtype=pool_mod.BITS_DTYPE[src_dtype])
+        x = pool_mod.bits_to_f64(bits, src_dtype)
+        return e4m3_mod.e4m3_encode(x * inv_scale_layer.astype(np.float64)[None])
+    monkeypatch.setattr(pool_mod.PoolModel, "_encode", encode64)
+    assert _any_fails(_fp8_pool_pins())
+
+
+def test_pool_fp8_layer_zero_scales_is_caught(monkeypatch):
+    # quantise every layer with layer 0's inverse scales
+    orig = pool_mod.PoolModel.append
+
+    def first_layer_scales(self, layer, k_bits, v_bits, src_dtype, slots):
+        if self.kv_dtype != "fp8":
+            return orig(self, layer, k_bits, v_bits, src_dtype, slots)
+        saved = self.k_inv_scale, self.v_inv_scale
+        self.k_inv_scale = np.broadcast_to(saved[0][:1], saved[0].shape)
+        self.v_inv_scale = np.broadcast_to(saved[1][:1], saved[1].shape)
+        try:
+            return orig(self, layer, k_bits, v_bits, src_dtype, slots)
+        finally:
+            self.k_inv_scale, self.v_inv_scale = saved
+    monkeypatch.setattr(pool_mod.PoolModel, "append", first_layer_scales)
+    assert _any_fails(_fp8_pool_pins())
