@@ -97,9 +97,12 @@ typedef struct {
   int32_t kv_dtype;       /* PKV_F32 / PKV_F16 / PKV_BF16 / PKV_FP8_E4M3 */
   void* k_cache;          /* device, layout above; may be NULL for a host-only pool */
   void* v_cache;          /* device, layout above; may be NULL for a host-only pool */
-  /* FP8 only (NULL otherwise): device fp32 [num_layers][num_kv_heads][head_dim].
-   * A stored code c stands for e4m3(c) * scale; appends encode
-   * x * inv_scale, where inv_scale is the caller's fp32 value of 1/scale. */
+  /* FP8 only (NULL otherwise): device fp32 [num_layers][num_kv_heads][head_dim],
+   * i.e. each array holds num_layers * num_kv_heads * head_dim floats (the
+   * kernels index it so; a shorter buffer is read past its end).  Per-channel
+   * scales (page "生成一个字…", section "再往后：压 KV 的三条路线"): a stored code c
+   * stands for e4m3(c) * scale; appends encode x * inv_scale, where inv_scale
+   * is the caller's fp32 value of 1/scale. */
   const float* k_scale;
   const float* v_scale;
   const float* k_inv_scale;
@@ -110,21 +113,32 @@ typedef struct {
 } kv_pool_desc;
 
 /* Bytes one of the two device buffers (K or V) of a pool must hold:
- * num_layers * num_blocks * num_kv_heads * block_size * head_dim * element size. */
+ * num_layers * num_blocks * num_kv_heads * block_size * head_dim * element size
+ * -- half the byte formula of page "生成一个字…" (opening section: 2 x layers x
+ * KV heads x head_dim x tokens x bytes) at num_blocks * block_size tokens. */
 pkv_status kv_pool_cache_bytes(const kv_pool_desc* desc, size_t* bytes_out);
 
-/* Create the host side of a pool.  Validates the descriptor (positive sizes, a
+/* Create the host side of a pool: the physical block pool of page "生成一个字…",
+ * section "PagedAttention：…" (fixed-size blocks anywhere in device memory,
+ * handed out on demand).  Validates the descriptor (positive sizes, a
  * permutation in free_order, scales present iff FP8).  All blocks start free
- * with reference count 0, queued in free_order.  *out receives the handle. */
+ * with reference count 0, queued in free_order.  *out receives the handle;
+ * on failure *out is set to NULL and nothing stays allocated. */
 pkv_status kv_pool_create(const kv_pool_desc* desc, kv_pool** out);
 /* Release the host side.  Device buffers are not touched.  NULL is a no-op. */
 void kv_pool_destroy(kv_pool* pool);
 
+/* Number of free physical blocks (same section: blocks are taken on demand,
+ * so this is what the pool can still give out).  PKV_E_INVAL on NULL. */
 pkv_status kv_pool_num_free(const kv_pool* pool, int32_t* out);
-/* Reference count of a physical block (0 = free). */
+/* Reference count of a physical block (0 = free): how many sequences hold it
+ * (same section: a shared prefix is stored once and counted; page
+ * "AI 陪读顶会论文（三）", section "PagedAttention 的破局哲学", innovation 3).
+ * PKV_E_INVAL for a block outside 0..num_blocks-1. */
 pkv_status kv_pool_refcount(const kv_pool* pool, int32_t block, int32_t* out);
-/* The free-block queue, front first: up to cap ids into out (host), the
- * queue length into *n_out. */
+/* The free-block queue, front first (the pages leave the free-block policy
+ * open; this library hands out the front and queues freed blocks at the
+ * back): up to cap ids into out (host), the queue length into *n_out. */
 pkv_status kv_pool_free_list(const kv_pool* pool, int32_t* out, int32_t cap, int32_t* n_out);
 
 /* ---- block tables (host only; page "生成一个字…", section "PagedAttention：…";

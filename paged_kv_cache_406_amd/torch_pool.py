@@ -17,14 +17,24 @@ class TorchKVPool:
         self.num_layers, self.num_kv_heads, self.head_dim = num_layers, num_kv_heads, head_dim
         self.block_size, self.num_blocks = block_size, num_blocks
         self.kv_dtype = B.DTYPE_CODE.get(kv_dtype, kv_dtype)
+        if self.kv_dtype == B.PKV_FP8_E4M3:
+            # the kernels index every scale array as [num_layers][num_kv_heads][head_dim]
+            want = (num_layers, num_kv_heads, head_dim)
+            for name, arr in (("k_scale", k_scale), ("v_scale", v_scale),
+                              ("k_inv_scale", k_inv_scale), ("v_inv_scale", v_inv_scale)):
+                if arr is None and name.endswith("inv_scale"):
+                    continue
+                if arr is None:
+                    raise ValueError("FP8 pools need k_scale and v_scale")
+                if np.shape(arr) != want:
+                    raise ValueError(f"{name} must have shape {want} (num_layers, num_kv_heads, head_dim), "
+                                     f"got {np.shape(arr)}")
         probe = B.make_desc(num_layers, num_kv_heads, head_dim, block_size, num_blocks, self.kv_dtype)
         self.cache_bytes = B.kv_pool_cache_bytes(probe)
         self.k_cache = torch.empty(self.cache_bytes, dtype=torch.uint8, device=device)
         self.v_cache = torch.empty(self.cache_bytes, dtype=torch.uint8, device=device)
         self.scales = {}
         if self.kv_dtype == B.PKV_FP8_E4M3:
-            if k_scale is None or v_scale is None:
-                raise ValueError("FP8 pools need k_scale and v_scale")
             k_scale = np.asarray(k_scale, dtype=np.float32)
             v_scale = np.asarray(v_scale, dtype=np.float32)
             if k_inv_scale is None:

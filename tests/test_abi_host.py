@@ -333,3 +333,17 @@ def test_common_prefix_of_fork_trees_matches_oracle(seed):
             P.block_table_common_prefix(h, [10 ** 6])
     finally:
         P.kv_pool_destroy(h)
+
+
+def test_torch_pool_rejects_scales_of_the_wrong_shape():
+    # the kernels index FP8 scales as [num_layers][num_kv_heads][head_dim]; one
+    # layer's scales for a two-layer pool would be read past their end
+    one = np.ones((1, 8, 128), np.float32)
+    two = np.ones((2, 8, 128), np.float32)
+    with pytest.raises(ValueError, match="shape"):
+        P.TorchKVPool(2, 8, 128, 16, 64, "fp8", device="cpu", k_scale=one, v_scale=two)
+    with pytest.raises(ValueError, match="shape"):
+        P.TorchKVPool(2, 8, 128, 16, 64, "fp8", device="cpu", k_scale=two, v_scale=two,
+                      k_inv_scale=two[:, :4])
+    with pytest.raises(ValueError, match="need"):
+        P.TorchKVPool(1, 8, 128, 16, 64, "fp8", device="cpu", k_scale=one)

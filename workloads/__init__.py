@@ -31,7 +31,9 @@ Draw order per workload: lengths, then the free-block permutation, from
 (so values depend only on logical coordinates, never on placement); q from
 ``default_rng([seed, 2])``; the shared prefix of c4 from
 ``default_rng([seed, 3])``; the token appended at decode step t from
-``default_rng([seed, 4, t])``.
+``default_rng([seed, 4, t])``.  A pool of several layers holds different
+values in each: sequence b's K/V in layer l > 0 come from
+``default_rng([seed, 5, l, b])`` (layer 0 keeps ``[seed, 1, b]``).
 """
 from dataclasses import dataclass, field, replace
 import math
@@ -185,6 +187,11 @@ def kv_tokens(w: Workload, stream, n_tokens: int, start: int = 0):
     k = rng.standard_normal(shape, dtype=np.float32) * np.float32(w.value_std)
     v = rng.standard_normal(shape, dtype=np.float32) * np.float32(w.value_std)
     return k[start:], v[start:]
+
+
+def kv_stream(b: int, layer: int = 0):
+    """Stream id of sequence b's K/V in one layer of the pool."""
+    return (1, b) if layer == 0 else (5, layer, b)
 
 
 def kv_tokens_bits(w: Workload, stream, n_tokens: int, start: int = 0):
