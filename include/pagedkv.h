@@ -388,6 +388,31 @@ pkv_status paged_attention_workspace_size(const kv_pool* pool, const paged_decod
 pkv_status paged_attention_decode(const kv_pool* pool, const paged_decode_args* args,
                                   pkv_stream stream);
 
+/* Size of the library's static decode workspace (64 MiB): device memory that
+ * every GPU the library runs on holds from the first use of the library's
+ * kernels until the process ends. */
+#define PKV_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+
+/* paged_attention_decode without a caller-owned workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same operation and result as
+ * paged_attention_decode; the split-K partials and merge records live in a
+ * static device array of PKV_STATIC_WORKSPACE_BYTES per GPU.  This call
+ * allocates nothing (no hipMalloc / hipFree, no allocating library routine);
+ * on its first use on a device it looks up that device's array address.
+ *  - args->workspace must be NULL and args->workspace_bytes 0 (else
+ *    PKV_E_INVAL).
+ *  - PKV_E_UNSUPPORTED, before any launch, when the call needs more than
+ *    PKV_STATIC_WORKSPACE_BYTES of workspace (paged_attention_workspace_size
+ *    gives the need; e.g. num_splits far above the automatic 4 per CU with a
+ *    large query group): use paged_attention_decode then.
+ *  - Every call on one GPU shares that GPU's array, which keeps the last
+ *    call's contents (the decode rewrites what it reads, so nothing needs
+ *    clearing).  Calls that may overlap on one GPU (different streams, or
+ *    host threads racing on one stream) race on the array: order them. */
+pkv_status paged_attention_decode_static(const kv_pool* pool, const paged_decode_args* args,
+                                         pkv_stream stream);
+
 /* paged_attention_decode, timed by its own kernels (same operation, same
  * pages).  kernel_events: host array of four hipEvent_t created with timing
  * enabled (caller-owned): [0] and [1] are recorded when the attention kernel

@@ -102,6 +102,7 @@ _SIGS = {
     "paged_kv_append_step": (c_i32, [P_pool, c_i32, c_vp, c_vp, c_i32, c_vp, c_i32, c_vp, c_vp, c_i32, c_vp]),
     "paged_attention_workspace_size": (c_i32, [P_pool, ctypes.POINTER(paged_decode_args), ctypes.POINTER(c_size)]),
     "paged_attention_decode": (c_i32, [P_pool, ctypes.POINTER(paged_decode_args), c_vp]),
+    "paged_attention_decode_static": (c_i32, [P_pool, ctypes.POINTER(paged_decode_args), c_vp]),
     "paged_attention_decode_timed": (c_i32, [P_pool, ctypes.POINTER(paged_decode_args), c_vp,
                                              ctypes.POINTER(c_vp), P_i32]),
     "pkv_last_error": (ctypes.c_char_p, []),
@@ -400,6 +401,15 @@ def paged_attention_workspace_size(pool, args) -> int:
 
 def paged_attention_decode(pool, args, stream=None) -> None:
     _check(_lib.paged_attention_decode(pool, ctypes.byref(args), _stream(stream)))
+
+
+PKV_STATIC_WORKSPACE_BYTES = 64 << 20
+
+
+def paged_attention_decode_static(pool, args, stream=None) -> None:
+    """paged_attention_decode on the library's static workspace (args must
+    carry no workspace)."""
+    _check(_lib.paged_attention_decode_static(pool, ctypes.byref(args), _stream(stream)))
 
 
 def paged_attention_decode_timed(pool, args, kernel_events, stream=None) -> int:

@@ -1578,14 +1578,16 @@ static pkv_status hip_fail(hipError_t e, const char* what) {
   return fail(PKV_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
+static constexpr int kMaxDevices = 64;
+
 static pkv_status device_cus(int* cus) {
   static std::mutex mu;
-  static std::vector<int> cache;
+  static int cache[kMaxDevices];   // fixed size: no host allocation on a launch path
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(PKV_E_UNSUPPORTED, "device index above 63");
   std::lock_guard<std::mutex> lk(mu);
-  if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
   if (!cache[dev]) {
     int n = 0;
     e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
@@ -1735,6 +1737,49 @@ static decode_fn pick_prefix(int kv, int d, int bs) {
     case PKV_FP8_E4M3: return d == 64 ? pick_prefix_bs<KV_FP8, 64>(bs) : pick_prefix_bs<KV_FP8, 128>(bs);
   }
   return nullptr;
+}
+
+// Workspace bytes of a decode call (arguments already checked).
+static pkv_status workspace_bytes_for(const kv_pool* pool, const paged_decode_args* a, size_t* bytes_out) {
+  const bool single = a->shared_prefix_blocks == 0 && (a->num_splits == 1 || a->max_blocks_per_seq == 0);
+  int cus = 0;
+  if ((!single && a->num_splits <= 1) || a->shared_prefix_blocks > 0) {
+    const pkv_status st = device_cus(&cus);
+    if (st != PKV_OK) return st;
+  }
+  int32_t rtiles = 0, chunks = 0;
+  if (a->shared_prefix_blocks > 0) prefix_plan(pool, a, cus, &rtiles, &chunks);
+  *bytes_out = workspace_layout(pool, a, single ? 0 : num_waves_for(a, cus), single, chunks).total;
+  return PKV_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Static decode workspace, for callers that cannot allocate device memory.
+// Every GPU the library runs on holds one copy of this array from the time
+// the code object is loaded until the process ends.  In host code `scratch`
+// names a host-side stand-in, not the device array: its device address is
+// looked up once per device with hipGetSymbolAddress and only that address
+// is ever passed to a kernel.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[PKV_STATIC_WORKSPACE_BYTES];
+
+static pkv_status scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices];   // per device, looked up on its first use
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(PKV_E_UNSUPPORTED, "device index above 63");
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(PKV_E_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return PKV_OK;
 }
 
 }  // namespace pkv
@@ -1911,16 +1956,7 @@ pkv_status paged_attention_workspace_size(const kv_pool* pool, const paged_decod
   if (!bytes_out) return fail(PKV_E_INVAL, "null argument");
   pkv_status st = check_decode(pool, a);
   if (st != PKV_OK) return st;
-  const bool single = a->shared_prefix_blocks == 0 && (a->num_splits == 1 || a->max_blocks_per_seq == 0);
-  int cus = 0;
-  if ((!single && a->num_splits <= 1) || a->shared_prefix_blocks > 0) {
-    st = device_cus(&cus);
-    if (st != PKV_OK) return st;
-  }
-  int32_t rtiles = 0, chunks = 0;
-  if (a->shared_prefix_blocks > 0) prefix_plan(pool, a, cus, &rtiles, &chunks);
-  *bytes_out = workspace_layout(pool, a, single ? 0 : num_waves_for(a, cus), single, chunks).total;
-  return PKV_OK;
+  return workspace_bytes_for(pool, a, bytes_out);
 }
 
 }  // extern "C"
@@ -2055,6 +2091,31 @@ extern "C" {
 
 pkv_status paged_attention_decode(const kv_pool* pool, const paged_decode_args* a, pkv_stream stream) {
   return decode_launch(pool, a, stream, nullptr, nullptr);
+}
+
+pkv_status paged_attention_decode_static(const kv_pool* pool, const paged_decode_args* a, pkv_stream stream) {
+  pkv_status st = check_decode(pool, a);
+  if (st != PKV_OK) return st;
+  if (a->workspace || a->workspace_bytes)
+    return fail(PKV_E_INVAL, "paged_attention_decode_static uses the library's static workspace: "
+                             "workspace must be NULL and workspace_bytes 0");
+  size_t need = 0;
+  st = workspace_bytes_for(pool, a, &need);
+  if (st != PKV_OK) return st;
+  if (need > PKV_STATIC_WORKSPACE_BYTES)
+    return fail(PKV_E_UNSUPPORTED, "this call needs " + std::to_string(need) +
+                                       " bytes of workspace, more than the static workspace's " +
+                                       std::to_string((size_t)PKV_STATIC_WORKSPACE_BYTES) +
+                                       ": use paged_attention_decode with a caller-owned workspace");
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != PKV_OK) return st;
+  // the decode rewrites every workspace record it reads on each call, so the
+  // previous call's contents need no clearing
+  paged_decode_args c = *a;
+  c.workspace = ws;
+  c.workspace_bytes = PKV_STATIC_WORKSPACE_BYTES;
+  return decode_launch(pool, &c, stream, nullptr, nullptr);
 }
 
 pkv_status paged_attention_decode_timed(const kv_pool* pool, const paged_decode_args* a, pkv_stream stream,

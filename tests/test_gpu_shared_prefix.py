@@ -39,7 +39,7 @@ CASES = {
 def _family(name, extra=0):
     w = CASES[name]
     d = wl.draw(w, extra_blocks=extra + 4)
-    st = FullState(w, d, range(w.batch))
+    st = FullState(w, d)
     return w, d, st
 
 
@@ -51,16 +51,16 @@ def test_shared_prefix_decode_parity(name):
         assert k == st.bm.common_prefix(st.oseqs) == w.prefix_len // w.block_size
         q = wl.q_bits(w)
         plain, ot, ol = st.decode(st.seqs, st.oseqs, q)
-        rows = range(w.batch)
-        st.check(plain, q, ot, ol, rows)
+        ref = st.reference(q, ot, ol)
+        st.check(plain, ref)
         for splits in (0, 1, 7):
             got, _, _ = st.decode(st.seqs, st.oseqs, q, shared=k, splits=splits)
-            st.check(got, q, ot, ol, rows)
+            st.check(got, ref)
             assert np.abs(got - plain).max() <= 2 * TOL[w.kv_dtype], splits
         # a shorter shared run than the common one is as valid
         if k > 1:
             got, _, _ = st.decode(st.seqs, st.oseqs, q, shared=k // 2)
-            st.check(got, q, ot, ol, rows)
+            st.check(got, ref)
     finally:
         st.close()
 
@@ -89,7 +89,7 @@ def test_shared_prefix_after_branch_step():
         k = P.block_table_common_prefix(h, branches)
         assert k == st.bm.common_prefix(obranches) == w.prefix_len // w.block_size
         got, ot, ol = st.decode(branches, obranches, qb, shared=k)
-        st.check(got, qb, ot, ol, range(w.batch))
+        st.check(got, st.reference(qb, ot, ol))
     finally:
         st.close()
 
