@@ -3,11 +3,11 @@
 One step is one pass of the whole decode hot path over one batch:
   1. host: reserve one slot per sequence (block_table_append_batch: on-demand
      blocks, copy-on-write of shared partial blocks),
-  2. one host->device copy of the step's metadata (slots, copy pairs, block
-     tables, context lengths) from pinned memory,
-  3. kv_pool_copy_blocks for the copy-on-write pairs,
-  4. paged_kv_append of the new token's K/V,
-  5. paged_attention_decode (range-split decode + log-sum-exp merge).
+  2. paged_kv_append_step: the new token's K/V into its slot, and the row's
+     table entry and length into the device-resident tables (forked
+     families, whose tables change every step, instead export and upload
+     the step's metadata, copy the copy-on-write blocks and append),
+  3. paged_attention_decode (range-split decode + log-sum-exp merge).
 Inputs (the cache and every step's q, k, v) are resident in HBM before the
 timed region starts.  Several independently placed copies of the cache are
 rotated so the working set is several times the 256 MB Infinity Cache.
@@ -17,12 +17,15 @@ bytes of the decode / step time).  ``roofline`` is the dominant kernel,
 decode_kernel, alone: its algorithmic bytes (everything the call must move
 except the output, which the merge writes) over its own launch duration,
 recorded by the kernel's start and end events on the launch stream;
-``decode_ms`` / ``decode_GBps`` are the whole call (decode_kernel +
-merge_kernel).  With a shared prefix the three kernels of the call are one
-unit and ``roofline`` is the call.  ``cpu_baseline`` is the CPU oracle timed
-on a bounded sample of the same workload.
+``roofline.call_*`` and ``decode_ms`` / ``decode_GBps`` are the whole call
+(decode_kernel + merge_kernel).  With a shared prefix the three kernels of
+the call are one unit and ``roofline`` is the call.  With the default
+workload (c3), ``targets`` holds the same figures for the 128K-context
+workloads (bf16 and FP8 KV), measured by shorter runs in the same process.
+``cpu_baseline`` is the CPU oracle timed on a bounded sample of the same
+workload.
 
-    python bench.py [--steps K] [--warmup W] [--workload c3]
+    python bench.py [--steps K] [--warmup W] [--workload c3] [--targets c5,c5_fp8]
 """
 import argparse
 import gc
@@ -253,13 +256,18 @@ def build_state(args, P, torch):
     streams = [(b, (1, b), int(L)) for b, L in enumerate(d.lengths)]
     if w.lengths_kind == "prefix":
         streams = [("prefix", (3,), w.prefix_len)] + [(b, (1, b), int(n)) for b, n in enumerate(d.suffix)]
-    for b, stream_id, L in streams:
-        kb, vb = wl.kv_tokens_bits(w, stream_id, L)
+    # the streams are drawn in parallel (NumPy releases the interpreter lock
+    # in the draws and conversions); results are used in stream order
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1))) as ex:
+        drawn = list(ex.map(lambda s: wl.kv_tokens_bits(w, s[1], s[2]), streams))
+    for (b, stream_id, L), (kb, vb) in zip(streams, drawn):
         if w.kv_dtype == "fp8":
             absmax_k = np.maximum(absmax_k, np.abs(wl.bits_as_f32(kb, w.src_dtype)).max(axis=0))
             absmax_v = np.maximum(absmax_v, np.abs(wl.bits_as_f32(vb, w.src_dtype)).max(axis=0))
         tdt = np.int16 if kb.dtype == np.uint16 else np.int32
         kv_cache[b] = (torch.from_numpy(kb.view(tdt)).cuda(), torch.from_numpy(vb.view(tdt)).cuda())
+    del drawn
     scales = {}
     if w.kv_dtype == "fp8":
         ks, _ = wl.fp8_scales(absmax_k)
@@ -486,6 +494,12 @@ def run(args):
     traffic = args.traffic * 1e9 if args.traffic else None
     if traffic is None and w.name in MEASURED_TRAFFIC and MEASURED_TRAFFIC[w.name][1] == kernels_sha():
         traffic = MEASURED_TRAFFIC[w.name][0]
+    traffic_source = None
+    if args.traffic:
+        traffic_source = "given on the command line (--traffic)"
+    elif traffic is not None:
+        traffic_source = (f"stored calibration, not read in this run: rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE "
+                          f"of this kernel source (kernels_sha {kernels_sha()}) scaled by a plain 1 GiB copy")
     achieved = s_bytes / (avg_dec_ms * 1e-3) / 1e9
     avg_kern_ms = float(np.mean(kern_ms))
     if prefix:
@@ -530,9 +544,15 @@ def run(args):
             "unit": "GB/s",
             "frac": round(r_achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
+            "traffic_source": traffic_source,
             "kernel": r_kernel,
             "launch_ms": round(r_ms, 5),
             "algorithmic_bytes": round(r_bytes),
+            # the whole paged_attention_decode call (every kernel it launches,
+            # all its algorithmic bytes), beside the dominant kernel alone
+            "call_ms": round(avg_dec_ms, 5),
+            "call_achieved": round(achieved, 2),
+            "call_frac": round(achieved / HBM_PEAK_GBS, 4),
         },
         "decode_timing": f"kernel durations recorded by the kernels themselves (hipExtLaunchKernelGGL "
                          f"start and end events, created with hipEventDisableSystemFence) on {len(dec_ms)} "
@@ -697,6 +717,9 @@ def main():
                     help="decode forked families without reading their common prefix once")
     ap.add_argument("--traffic", type=float, default=None,
                     help="HBM bytes per decode_kernel launch from rocprofv3 counters (GB)")
+    ap.add_argument("--targets", default="c5,c5_fp8",
+                    help="with the default c3 workload, also measure these workloads (comma list; '' for none)")
+    ap.add_argument("--target-steps", type=int, default=24)
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
     ap.add_argument("--read-probe", type=int, default=0,
@@ -714,6 +737,26 @@ def main():
               "multi-GPU runs are not part of this benchmark", file=sys.stderr)
         sys.exit(2)
     res, w, d, scales = run(args)
+    # the other configurations the 70 % target is stated on (128K context,
+    # bf16 and FP8 KV), measured in the same process with the same timing:
+    # a shorter run of each, decode kernel and whole call
+    if args.targets and args.workload == "c3":
+        res["targets"] = {}
+        for name in [x for x in args.targets.split(",") if x]:
+            sub = argparse.Namespace(**vars(args))
+            sub.workload, sub.steps, sub.warmup, sub.replicas = name, args.target_steps, 3, 0
+            r, _, _, _ = run(sub)
+            res["targets"][name] = {
+                "workload": r["config"]["workload"], "steps": r["steps"], "ms_per_step": r["ms_per_step"],
+                "value_GBps": r["value"], "decode_kernel_ms": r["roofline"]["launch_ms"],
+                "decode_kernel_bytes": r["roofline"]["algorithmic_bytes"],
+                "decode_kernel_GBps": r["roofline"]["achieved"], "decode_kernel_frac": r["roofline"]["frac"],
+                "call_ms": r["roofline"]["call_ms"], "call_GBps": r["roofline"]["call_achieved"],
+                "call_frac": r["roofline"]["call_frac"], "seq_heads_per_s": r["decode_seq_heads_per_s"],
+                "traffic": r["roofline"]["traffic"], "traffic_source": r["roofline"]["traffic_source"],
+            }
+            log(f"{name}: decode_kernel {r['roofline']['launch_ms']:.4f} ms, frac {r['roofline']['frac']:.3f}; "
+                f"call {r['roofline']['call_ms']:.4f} ms, frac {r['roofline']['call_frac']:.3f}")
     # context for the roofline: what a plain streaming read of 2 GiB reaches
     # on this device (pkv_hbm_read_probe, median of 10 calls)
     res["hbm_read_probe_GBps"] = round(read_probe(1 << 31, 10), 1)
