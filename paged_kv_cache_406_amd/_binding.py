@@ -5,13 +5,19 @@ can be given as integers or as torch tensors (their ``data_ptr()``); streams
 default to torch's current stream on the current device.  A negative status
 raises ``PagedKVError`` (``PagedKVOOM`` for pool exhaustion) with the
 library's message.
+
+The environment variable PKV_LIBRARY names another build of the library to
+load instead of the in-tree libpagedkv.so (the tests use it for the host-only
+build under AddressSanitizer and UndefinedBehaviorSanitizer).  An entry point
+that build does not export raises PagedKVError when called.
 """
 import ctypes
 import os
 
 import numpy as np
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
+_LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                           "libpagedkv.so")
 
 PKV_OK, PKV_E_INVAL, PKV_E_OOM, PKV_E_DTYPE, PKV_E_UNSUPPORTED, PKV_E_HIP, PKV_E_INTERNAL = 0, -1, -2, -3, -4, -5, -6
 PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2, 3
@@ -107,8 +113,24 @@ _SIGS = {
                                              ctypes.POINTER(c_vp), P_i32]),
     "pkv_last_error": (ctypes.c_char_p, []),
 }
+class _NotInThisBuild:
+    """Stands in for an entry point the loaded build does not export."""
+
+    def __init__(self, name):
+        self.name = name
+
+    def __call__(self, *args):
+        raise PagedKVError(PKV_E_UNSUPPORTED, f"{self.name} is not in this build of the library ({_LIB_PATH})")
+
+
 for _name, (_res, _args) in _SIGS.items():
-    _f = getattr(_lib, _name)
+    try:
+        _f = getattr(_lib, _name)
+    except AttributeError:
+        if not os.environ.get("PKV_LIBRARY"):
+            raise          # the in-tree library exports every entry point
+        setattr(_lib, _name, _NotInThisBuild(_name))
+        continue
     _f.restype = _res
     _f.argtypes = _args
 

@@ -1,6 +1,7 @@
 """Builds libpagedkv.so (host block tables + gfx950 HIP kernels) in-tree.
 
-    python paged_kv_cache_406_amd/build.py
+    python paged_kv_cache_406_amd/build.py                    # the library
+    python paged_kv_cache_406_amd/build.py --host-sanitized   # host part under ASan + UBSan
 
 The host part is compiled with g++, the kernels with hipcc for gfx950, and
 both are linked by hipcc into ``paged_kv_cache_406_amd/libpagedkv.so``.
@@ -58,5 +59,26 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+SANITIZED_LIB = os.path.join(ROOT, "_build", "libpagedkv_host_asan.so")
+SANITIZE_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-std=c++17", "-fPIC", "-Wall", "-Wextra",
+                  "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined"]
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """The host part alone (block tables, prefix cache) built with g++ under
+    AddressSanitizer and UndefinedBehaviorSanitizer, for CPU tests: load it
+    with PKV_LIBRARY=<path> and the sanitizer runtime preloaded
+    (LD_PRELOAD=$(g++ -print-file-name=libasan.so)).  It has no device code."""
+    os.makedirs(os.path.dirname(SANITIZED_LIB), exist_ok=True)
+    tmp_lib = SANITIZED_LIB + ".tmp"
+    _run(["g++", *SANITIZE_FLAGS, "-I", INCLUDE, "-shared", os.path.join(CSRC, "pool.cpp"),
+          os.path.join(CSRC, "prefix_cache.cpp"), "-o", tmp_lib], verbose)
+    os.replace(tmp_lib, SANITIZED_LIB)
+    return SANITIZED_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--host-sanitized" in sys.argv:
+        print(build_host_sanitized(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

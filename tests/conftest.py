@@ -11,6 +11,9 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: long-running CPU test")
+    config.addinivalue_line("markers", "device_code: calls the library's device entry points (host-side "
+                                       "checks only, no GPU needed); needs the full library, not the "
+                                       "host-only sanitizer build")
 
 
 def pytest_collection_modifyitems(config, items):

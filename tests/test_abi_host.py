@@ -24,6 +24,7 @@ def _declared_functions():
     return sorted(set(n for n in names if n not in ("if", "defined")))
 
 
+@pytest.mark.device_code
 def test_header_symbols_exported():
     declared = _declared_functions()
     assert len(declared) >= 17
@@ -189,7 +190,15 @@ def test_errors_and_strong_guarantee():
             P.block_table_free(h, s)
         with pytest.raises(P.PagedKVError):
             P.block_table_fork(h, s)
-        # device calls on a pool without device buffers are rejected on the host
+    finally:
+        P.kv_pool_destroy(h)
+
+
+@pytest.mark.device_code
+def test_device_calls_on_a_host_only_pool_are_rejected():
+    # device calls on a pool without device buffers are rejected on the host
+    h = P.kv_pool_create(P.make_desc(1, 1, 64, 4, 4, "f32"))
+    try:
         with pytest.raises(P.PagedKVError):
             P.kv_pool_copy_blocks(h, 0, 1, stream=0)
         with pytest.raises(P.PagedKVError):
@@ -217,6 +226,7 @@ def test_descriptor_validation():
     P.kv_pool_destroy(h)
 
 
+@pytest.mark.device_code
 def test_decode_argument_validation_on_host():
     # a pool with (fake, never dereferenced) device pointers: every check below
     # fails before any launch
@@ -256,6 +266,7 @@ def test_decode_argument_validation_on_host():
         P.kv_pool_destroy(h)
 
 
+@pytest.mark.device_code
 def test_one_hip_runtime_in_process():
     # Loading the library must not bring a second HIP runtime into a process
     # that also uses torch (two runtimes: the second one finds no device).
@@ -289,6 +300,7 @@ def test_decode_args_keep_their_tensors_alive():
     assert all(r() is None for r in refs)
 
 
+@pytest.mark.device_code
 def test_metadata_upload_rejects_bad_arguments_on_host():
     # null and misaligned arguments are refused before any HIP call
     with pytest.raises(P.PagedKVError):
