@@ -338,8 +338,11 @@ typedef struct {
   const void* q;                /* device [B][Hq][head_dim], 16-byte aligned */
   int32_t q_dtype;              /* PKV_F32 for an fp32 pool, PKV_F16 for fp16,
                                    PKV_BF16 for bf16 and FP8 pools */
-  const int32_t* block_tables;  /* device int32 [B][max_blocks_per_seq] */
-  const int32_t* context_lens;  /* device int32 [B]: tokens including the new one */
+  int32_t* block_tables;        /* device int32 [B][max_blocks_per_seq]; written only by a
+                                   fused append (below) */
+  int32_t* context_lens;        /* device int32 [B]: tokens including the new one (with a
+                                   fused append: the cached tokens before it; the call
+                                   then adds one) */
   float scale;                  /* multiplies q.k; 1/sqrt(head_dim) by convention */
   void* out;                    /* device [B][Hq][head_dim], 16-byte aligned */
   int32_t out_dtype;            /* PKV_F32 (recommended), PKV_F16 or PKV_BF16 */
@@ -361,6 +364,27 @@ typedef struct {
                                    "PagedAttention：…", and page "AI 陪读顶会论文（三）",
                                    innovation 3: a shared prefix is stored once;
                                    here it is also read once per call. */
+  /* Fused append (optional; new_k == NULL: off).  The step's new token is
+   * appended and attended in the same call (page "AI 陪读顶会论文（三）", section
+   * "为什么自回归解码…必须使用 KV Cache": each step appends the new token's k, v
+   * and its query attends every cached token, itself included).  Then
+   * context_lens[b] = L counts the cached tokens before the new one, and the
+   * call:
+   *  - attends the L cached tokens and the new token (k, v from new_k, new_v,
+   *    quantised like the pool for FP8; the window, if set, ends at the new
+   *    token), combining the new token with the rest by the log-sum-exp merge;
+   *  - writes the new token into the pool at new_slots[b] (as paged_kv_append
+   *    does), block_tables[b][L / block_size] = new_slots[b] / block_size
+   *    and context_lens[b] = L + 1, after every read of them.
+   * new_slots[b] is the slot block_table_append gave (its copy-on-write
+   * pairs copied first); a slot outside the pool means row b has no new
+   * token (nothing written, L tokens attended).  L / block_size must be below
+   * max_blocks_per_seq, else the table entry and length are not written.
+   * Same result as paged_kv_append followed by paged_attention_decode. */
+  const void* new_k;            /* device [B][Hkv][head_dim], 16-byte aligned */
+  const void* new_v;            /* device [B][Hkv][head_dim], 16-byte aligned */
+  int32_t new_dtype;            /* the pool's dtype, or f32 / f16 / bf16 into an FP8 pool */
+  const int64_t* new_slots;     /* device or page-locked host [B] */
 } paged_decode_args;
 
 /* Workspace paged_attention_decode needs for these arguments (0 for a single

@@ -71,7 +71,8 @@ class paged_decode_args(ctypes.Structure):
                 ("q", c_vp), ("q_dtype", c_i32),
                 ("block_tables", c_vp), ("context_lens", c_vp),
                 ("scale", c_float), ("out", c_vp), ("out_dtype", c_i32),
-                ("workspace", c_vp), ("workspace_bytes", c_size), ("shared_prefix_blocks", c_i32)]
+                ("workspace", c_vp), ("workspace_bytes", c_size), ("shared_prefix_blocks", c_i32),
+                ("new_k", c_vp), ("new_v", c_vp), ("new_dtype", c_i32), ("new_slots", c_vp)]
 
 
 P_pool = c_vp
@@ -398,7 +399,11 @@ def paged_kv_append_step(pool, layer, d_k, d_v, src_dtype, slots, n, d_tables, d
 
 def make_decode_args(layer, batch, num_q_heads, max_blocks_per_seq, q, q_dtype, block_tables,
                      context_lens, scale, out, out_dtype="f32", sliding_window=0, num_splits=0,
-                     workspace=None, workspace_bytes=0, shared_prefix_blocks=0):
+                     workspace=None, workspace_bytes=0, shared_prefix_blocks=0,
+                     new_k=None, new_v=None, new_dtype=None, new_slots=None):
+    """Arguments of paged_attention_decode.  new_k / new_v / new_slots (with
+    new_dtype, default q_dtype) turn on the fused append: context_lens then
+    counts the cached tokens before the step's new token."""
     a = paged_decode_args()
     a.layer, a.batch, a.num_q_heads = layer, batch, num_q_heads
     a.max_blocks_per_seq, a.sliding_window, a.num_splits = max_blocks_per_seq, sliding_window, num_splits
@@ -408,10 +413,12 @@ def make_decode_args(layer, batch, num_q_heads, max_blocks_per_seq, q, q_dtype, 
     a.out, a.out_dtype = _ptr(out), DTYPE_CODE.get(out_dtype, out_dtype)
     a.workspace, a.workspace_bytes = _ptr(workspace), workspace_bytes
     a.shared_prefix_blocks = shared_prefix_blocks
+    a.new_k, a.new_v, a.new_slots = _ptr(new_k), _ptr(new_v), _ptr(new_slots)
+    a.new_dtype = DTYPE_CODE.get(new_dtype, new_dtype) if new_dtype is not None else a.q_dtype
     # the struct holds raw device addresses: keep the tensors they came from
     # alive as long as the struct, or torch may hand their memory to the next
     # allocation before the decode is launched
-    a._refs = (q, block_tables, context_lens, out, workspace)
+    a._refs = (q, block_tables, context_lens, out, workspace, new_k, new_v, new_slots)
     return a
 
 

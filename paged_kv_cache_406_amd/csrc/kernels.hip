@@ -166,10 +166,63 @@ struct AppendParams {
   int32_t max_blocks;
 };
 
+// One token's K group c (X channels, 16 bytes in the pool) and its X V
+// elements (dims e * D/X + c) of KV head h, from source row `row` (element
+// index of the token's head row in k / v), into block blk at offset off of
+// `layer`.
 template <int KV, int SRC>
-__global__ __launch_bounds__(256) void append_kernel(AppendParams P) {
+__device__ __forceinline__ void store_token_chunk(uint8_t* kc, uint8_t* vc, const uint8_t* k, const uint8_t* v,
+                                                  const float* k_inv, const float* v_inv, int64_t num_blocks,
+                                                  int hkv, int d, int bs, int layer, int64_t row, int c, int h,
+                                                  int64_t blk, int off) {
   constexpr int EB = Elem<KV>::bytes;
   constexpr int X = 16 / EB;
+  const int chunks = d / X;
+  const int64_t tile = ((int64_t)layer * num_blocks + blk) * hkv + h;
+  const int64_t src0 = row + (int64_t)c * X;       // this thread's K chunk
+  uint8_t* kdst = kc + ((tile * (d / X) + c) * bs + off) * 16;
+  // V runs of vt tokens, channel-major inside a run: element dim of this
+  // token sits vt elements after element dim - 1.  The thread's e-th V
+  // element is dim e * chunks + c, so the lanes of one store instruction
+  // cover consecutive dims, and the dims that share a cache line are written
+  // by one instruction.
+  const int vt = v_run(bs, SubTile<KV>::TT);
+  uint8_t* vdst = vc + (tile * d * bs + (int64_t)(off / vt) * d * vt + off % vt) * EB;
+  if constexpr (KV == SRC) {
+    // non-temporal stores: the cache lines this token touches (one 16-byte
+    // K group, D two- or four-byte V elements in bs-element rows) are not
+    // read again by this kernel
+    const u32x4 kv = *reinterpret_cast<const u32x4*>(k + src0 * EB);
+    __builtin_nontemporal_store(kv, reinterpret_cast<u32x4*>(kdst));
+#pragma unroll
+    for (int e = 0; e < X; ++e) {
+      const int64_t dim = (int64_t)e * chunks + c;
+      uint8_t* dst = vdst + dim * vt * EB;
+      if constexpr (EB == 4)
+        __builtin_nontemporal_store(reinterpret_cast<const uint32_t*>(v)[row + dim], reinterpret_cast<uint32_t*>(dst));
+      else if constexpr (EB == 2)
+        __builtin_nontemporal_store(reinterpret_cast<const uint16_t*>(v)[row + dim], reinterpret_cast<uint16_t*>(dst));
+    }
+  } else {
+    static_assert(KV == KV_FP8, "only same-dtype copy or FP8 quantisation");
+    const int64_t s0 = ((int64_t)layer * hkv + h) * d;   // channel scales of (layer, head)
+    uint32_t kw[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < X; ++e) {
+      const int kd = c * X + e;
+      const float kx = src_to_f32<SRC>(k, row + kd) * k_inv[s0 + kd];
+      kw[e >> 2] |= f32_to_e4m3(kx) << (8 * (e & 3));
+      const int64_t vd = (int64_t)e * chunks + c;
+      const float vx = src_to_f32<SRC>(v, row + vd) * v_inv[s0 + vd];
+      __builtin_nontemporal_store((uint8_t)f32_to_e4m3(vx), vdst + vd * vt);
+    }
+    __builtin_nontemporal_store(u32x4{kw[0], kw[1], kw[2], kw[3]}, reinterpret_cast<u32x4*>(kdst));
+  }
+}
+
+template <int KV, int SRC>
+__global__ __launch_bounds__(256) void append_kernel(AppendParams P) {
+  constexpr int X = 16 / Elem<KV>::bytes;
   const int chunks = P.d / X;
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = (int64_t)P.n * P.hkv * chunks;
@@ -202,47 +255,9 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams P) {
       P.lens[i] = pos + 1;
     }
   }
-  const int64_t tile = ((int64_t)P.layer * P.num_blocks + blk) * P.hkv + h;
   const int64_t row = (i * P.hkv + h) * P.d;       // element index of the token's (head) row
-  const int64_t src0 = row + (int64_t)c * X;       // this thread's K chunk
-  uint8_t* kdst = P.kc + ((tile * (P.d / X) + c) * P.bs + off) * 16;
-  // V runs of vt tokens, channel-major inside a run: element dim of this
-  // token sits vt elements after element dim - 1.  The thread's e-th V
-  // element is dim e * chunks + c, so the lanes of one store instruction
-  // cover consecutive dims, and the dims that share a cache line are written
-  // by one instruction.
-  const int vt = v_run(P.bs, SubTile<KV>::TT);
-  uint8_t* vdst = P.vc + (tile * P.d * P.bs + (int64_t)(off / vt) * P.d * vt + off % vt) * EB;
-  if constexpr (KV == SRC) {
-    // non-temporal stores: the cache lines this token touches (one 16-byte
-    // K group, D two- or four-byte V elements in bs-element rows) are not
-    // read again by this kernel
-    const u32x4 kv = *reinterpret_cast<const u32x4*>(P.k + src0 * EB);
-    __builtin_nontemporal_store(kv, reinterpret_cast<u32x4*>(kdst));
-#pragma unroll
-    for (int e = 0; e < X; ++e) {
-      const int64_t dim = (int64_t)e * chunks + c;
-      uint8_t* dst = vdst + dim * vt * EB;
-      if constexpr (EB == 4)
-        __builtin_nontemporal_store(reinterpret_cast<const uint32_t*>(P.v)[row + dim], reinterpret_cast<uint32_t*>(dst));
-      else if constexpr (EB == 2)
-        __builtin_nontemporal_store(reinterpret_cast<const uint16_t*>(P.v)[row + dim], reinterpret_cast<uint16_t*>(dst));
-    }
-  } else {
-    static_assert(KV == KV_FP8, "only same-dtype copy or FP8 quantisation");
-    const int64_t s0 = ((int64_t)P.layer * P.hkv + h) * P.d;   // channel scales of (layer, head)
-    uint32_t kw[4] = {0, 0, 0, 0};
-#pragma unroll
-    for (int e = 0; e < X; ++e) {
-      const int kd = c * X + e;
-      const float kx = src_to_f32<SRC>(P.k, row + kd) * P.k_inv[s0 + kd];
-      kw[e >> 2] |= f32_to_e4m3(kx) << (8 * (e & 3));
-      const int64_t vd = (int64_t)e * chunks + c;
-      const float vx = src_to_f32<SRC>(P.v, row + vd) * P.v_inv[s0 + vd];
-      __builtin_nontemporal_store((uint8_t)f32_to_e4m3(vx), vdst + vd * vt);
-    }
-    __builtin_nontemporal_store(u32x4{kw[0], kw[1], kw[2], kw[3]}, reinterpret_cast<u32x4*>(kdst));
-  }
+  store_token_chunk<KV, SRC>(P.kc, P.vc, P.k, P.v, P.k_inv, P.v_inv, P.num_blocks, P.hkv, P.d, P.bs, P.layer,
+                             row, c, h, blk, off);
 }
 
 // ---------------------------------------------------------------------------
@@ -307,6 +322,27 @@ struct DecodeParams {
   // range mode: 1 when the context lengths are also kept in LDS, after the
   // unit prefix sums (a piece's start then reads no global memory)
   int32_t lens_in_lds;
+  // every (KV head, sequence) pair leaves a partial (o, max, sum) for
+  // merge_kernel, also when one wavefront held all of it: with a shared
+  // prefix, and with a fused append
+  int32_t allpart;
+  // fused append (fused = 1): lens[b] counts the cached tokens before the new
+  // one.  The decode attends the cached tokens (the window counted over all
+  // L + 1); merge_kernel folds in the new token as one more partial (scores
+  // from new_k, values from new_v, quantised like the pool for FP8), writes
+  // it into the pool at new_slots[b], writes the row's table entry and
+  // lens[b] = L + 1.  A row whose slot is outside the pool has no new token.
+  int32_t fused;
+  int32_t new_src;         // dtype of new_k / new_v
+  int32_t kv_dtype;        // the pool's
+  int32_t block_size;
+  const uint8_t* new_k;    // [B][Hkv][D]
+  const uint8_t* new_v;
+  const int64_t* new_slots;  // [B], device or page-locked host memory
+  const float* k_inv;      // FP8: inverse scales used to encode
+  const float* v_inv;
+  int32_t* tables_w;       // the same tables and lengths, written by merge_kernel
+  int32_t* lens_w;
 };
 
 // Which piece an LDS staging slot of the decode holds (48 bytes, so that
@@ -332,7 +368,9 @@ __device__ __forceinline__ void extent_of(const DecodeParams& P, int32_t L, int3
                                           int32_t* first_out, int32_t* nunits_out) {
   const int32_t cap = P.max_blocks * BS;
   L = L < 0 ? 0 : (L > cap ? cap : L);
-  const int32_t lo = P.window > 0 ? (L - P.window > 0 ? L - P.window : 0) : 0;
+  // with a fused append the window ends at the new token, one past L
+  const int32_t Lw = L + (P.fused ? 1 : 0);
+  const int32_t lo = P.window > 0 ? (Lw - P.window > 0 ? Lw - P.window : 0) : 0;
   // with a shared prefix (no window) the blocks before `shared` are
   // prefix_kernel's
   const int32_t first = P.shared > 0 ? P.shared : lo / BS;
@@ -890,7 +928,7 @@ struct Decoder {
     v_scales(P, s.g, kg, vsc);
     const int G = P.group;
     const bool full = beg == s.start && end == s.start + s.nb;
-    if (full && P.shared) {
+    if (full && P.allpart) {
       // the whole of the pair's own part: its partial goes to the slot after
       // the prefix chunks, and merge_kernel joins the two (job.w = 1)
       if (lane == 0) P.ws_job[(int64_t)s.g * P.batch + s.b] = make_int4(0, 0, 0, 1);
@@ -1331,7 +1369,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     int32_t L, lo, first, nu;
     seq_extent<BS, U>(P, b, &L, &lo, &first, &nu);
     if (nu == 0) {
-      write_zero_rows<D>(P, b, g, lane);
+      // nothing cached to attend: zeros, or (fused append) the new token
+      // alone, which merge_kernel writes
+      if (!P.allpart) write_zero_rows<D>(P, b, g, lane);
+      else if (lane == 0) P.ws_job[w] = make_int4(0, 0, 0, 0);
       return;
     }
     Dec::stream(P, nullptr, 0, 0, 0, 0, 0, 0, g, b, nullptr);
@@ -1347,9 +1388,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int64_t seg = w; seg < nseg; seg += launched) {
     const int b = (int)(seg % P.batch);
     if (C[b + 1] == C[b]) {
-      // nothing of its own to attend: zeros, or (shared prefix) the merge of
-      // the prefix partials alone, written by merge_kernel
-      if (!P.shared) write_zero_rows<D>(P, b, (int)(seg / P.batch), lane);
+      // nothing of its own to attend: zeros, or (shared prefix, fused append)
+      // the merge of the prefix partials and the new token alone, written by
+      // merge_kernel
+      if (!P.allpart) write_zero_rows<D>(P, b, (int)(seg / P.batch), lane);
       if (lane == 0) P.ws_job[seg] = make_int4(0, 0, 0, 0);
     }
   }
@@ -1390,6 +1432,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   Dec::prefix_group(P, g, (int)(rem / P.pre_chunks), (int)(rem % P.pre_chunks), stage);
 }
 
+// Source element idx of new_k / new_v as fp32 (run-time source dtype).
+__device__ __forceinline__ float new_src_value(int src, const uint8_t* p, int64_t idx) {
+  if (src == PKV_F32) return src_to_f32<KV_F32>(p, idx);
+  if (src == PKV_F16) return src_to_f32<KV_F16>(p, idx);
+  return src_to_f32<KV_BF16>(p, idx);
+}
+
+// The value the pool holds for source element x of channel (layer, head)
+// offset s: x itself, or (FP8) the E4M3 code of x * inv_scale decoded and
+// times the scale -- what the decode reads back.
+__device__ __forceinline__ float pool_value(const DecodeParams& P, float x, const float* inv, const float* scale,
+                                            int64_t s) {
+  if (P.kv_dtype != PKV_FP8_E4M3) return x;
+  const uint32_t code = f32_to_e4m3(x * inv[s]);
+  const bf16x2 w = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(code, 1.0f, false);
+  return (float)w[0] * scale[s];
+}
+
+// Fused append: write the new token's 16-byte K group c and its V elements
+// of KV head h into the pool (run-time pool and source dtypes).
+__device__ __forceinline__ void store_new_token(const DecodeParams& P, int b, int h, int c, int64_t blk, int off,
+                                                int D) {
+  uint8_t* kc = const_cast<uint8_t*>(P.kc);
+  uint8_t* vc = const_cast<uint8_t*>(P.vc);
+  const int64_t row = ((int64_t)b * P.hkv + h) * D;
+#define PKV_STORE(KVT, SRCT)                                                                               \
+  store_token_chunk<KVT, SRCT>(kc, vc, P.new_k, P.new_v, P.k_inv, P.v_inv, P.num_blocks, P.hkv, D,          \
+                               P.block_size, P.layer, row, c, h, blk, off)
+  switch (P.kv_dtype) {
+    case PKV_F32: PKV_STORE(KV_F32, KV_F32); break;
+    case PKV_F16: PKV_STORE(KV_F16, KV_F16); break;
+    case PKV_BF16: PKV_STORE(KV_BF16, KV_BF16); break;
+    default:
+      if (P.new_src == PKV_F32) PKV_STORE(KV_FP8, KV_F32);
+      else if (P.new_src == PKV_F16) PKV_STORE(KV_FP8, KV_F16);
+      else PKV_STORE(KV_FP8, KV_BF16);
+  }
+#undef PKV_STORE
+}
+
 // Log-sum-exp merge of the pieces of a split (KV head, sequence).  Workgroup
 // (seg, y) of 256 threads owns a contiguous share of the G * D/4 output
 // positions (head h, 4 dims) of sequence-head seg; TPP threads share a
@@ -1400,30 +1482,60 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // exchanges, then the rescaled sums by a butterfly that leaves the same bits
 // in every lane of a position (deterministic).  Piece p of a job whose first
 // piece is in range w0 is in slot (w0, first) for p = 0 and (w0 + p, 0) after.
+//
+// With a fused append the new token is one more partial of every (sequence,
+// head): o = its V row, max = its score, sum = 1.  Its scores are computed
+// first (one wavefront per head, lanes over the dims), then folded in by the
+// first thread of each position; the token is written into the pool (K, V
+// of this KV head) and, by one workgroup per sequence, into the row's table
+// entry and length, after the outputs.
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeParams P) {
   constexpr int NPC = 8;   // pieces per thread per batch
   const int64_t seg = blockIdx.x;
+  const int b = (int)(seg % P.batch), g = (int)(seg / P.batch);
+  const int G = P.group;
+  const int tid = threadIdx.x;
+  __shared__ float s_new[16];          // log2-domain score of the new token, per head of the group
+  __shared__ int64_t slot_sh;
+  int64_t slot = -1;
+  if (P.fused) {
+    const int lane = tid & 63, wv = tid >> 6;
+    if (tid == 0) slot_sh = __hip_atomic_load(P.new_slots + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const int qdt = P.kv_dtype == PKV_FP8_E4M3 ? PKV_BF16 : P.kv_dtype;
+    const int64_t s0 = ((int64_t)P.layer * P.hkv + g) * D;   // channel scales of (layer, KV head)
+    const int64_t krow = ((int64_t)b * P.hkv + g) * D;
+    for (int h = wv; h < G; h += 4) {
+      const int64_t qrow = ((int64_t)b * P.hq + (int64_t)g * G + h) * D;
+      float acc = 0.f;
+      for (int d = lane; d < D; d += 64) {
+        const float k = pool_value(P, new_src_value(P.new_src, P.new_k, krow + d), P.k_inv, P.k_scale, s0 + d);
+        acc += new_src_value(qdt, P.q, qrow + d) * k;
+      }
+      for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+      if (lane == 0) s_new[h] = acc * P.scale_log2;
+    }
+    __syncthreads();
+    slot = slot_sh;
+  }
+  const bool has_new = P.fused && slot >= 0 && slot < P.num_blocks * P.block_size;
   const int4 job = P.ws_job[seg];
   const int npieces = job.y;
-  if (npieces == 0 && !P.shared) return;
+  if (npieces == 0 && !P.allpart) return;
   const int64_t w0 = job.x;
   const int first_which = job.z;
-  const int b = (int)(seg % P.batch), g = (int)(seg / P.batch);
   constexpr int D4 = D / 4;
-  const int G = P.group;
   const int NP = G * D4;
   const int npg = (NP + gridDim.y - 1) / gridDim.y;
   const int pos0 = blockIdx.y * npg;
   const int pos1 = min(NP, pos0 + npg);
   int tpp = 1;
   while (tpp * 2 * npg <= 256 && tpp < 64) tpp *= 2;   // threads per position (lanes of one wavefront)
-  const int tid = threadIdx.x;
   const int sub = tid % tpp;
   for (int pos = pos0 + tid / tpp; pos < pos1; pos += 256 / tpp) {
     const int h = pos / D4;
     const int d4 = (pos % D4) * 4;
-    auto slot = [&](int pc) -> int64_t { return ((w0 + pc) * 2 + (pc == 0 ? first_which : 0)) * G + h; };
+    auto slot_of = [&](int pc) -> int64_t { return ((w0 + pc) * 2 + (pc == 0 ? first_which : 0)) * G + h; };
     float M = -INFINITY, Ls = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int base = sub; base < npieces; base += NPC * tpp) {
@@ -1433,7 +1545,7 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams P) {
       for (int k = 0; k < NPC; ++k) {
         const int pc = base + k * tpp;
         if (pc < npieces) {
-          const int64_t sl = slot(pc);
+          const int64_t sl = slot_of(pc);
           ml[k] = *reinterpret_cast<const f32x2*>(P.ws_ml + sl * 2);
           o[k] = *reinterpret_cast<const f32x4*>(P.ws_o + sl * D + d4);
         } else {
@@ -1459,7 +1571,7 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams P) {
     // the prefix partials of this (sequence, head), and (job.w) the partial
     // of its own part when one wavefront held all of it: same fold, also up
     // to NPC partials per thread per round trip
-    if (P.shared) {
+    if (P.allpart) {
       const int64_t bhq = (int64_t)P.batch * P.hq;
       const int64_t hrow = (int64_t)b * P.hq + (int64_t)g * G + h;
       const int nslots = P.pre_chunks + (job.w ? 1 : 0);
@@ -1494,6 +1606,23 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams P) {
         M = Mb;
       }
     }
+    // the new token: one more partial (its V row, its score, sum 1), folded
+    // in by one thread of the position
+    if (has_new && sub == 0) {
+      const int64_t s0 = ((int64_t)P.layer * P.hkv + g) * D;
+      const int64_t vrow = ((int64_t)b * P.hkv + g) * D;
+      f32x4 vn;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        vn[e] = pool_value(P, new_src_value(P.new_src, P.new_v, vrow + d4 + e), P.v_inv, P.v_scale, s0 + d4 + e);
+      const float sn = s_new[h];
+      const float Mb = fmaxf(M, sn);
+      const float r = __builtin_amdgcn_exp2f(M - Mb);     // M = -inf: 0
+      const float wt = __builtin_amdgcn_exp2f(sn - Mb);
+      acc = acc * r + vn * wt;
+      Ls = Ls * r + wt;
+      M = Mb;
+    }
     // combine the tpp threads of the position: common max, rescale, sum
     float Mall = M;
     for (int off = 1; off < tpp; off <<= 1) Mall = fmaxf(Mall, __shfl_xor(Mall, off));
@@ -1508,6 +1637,21 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams P) {
     if (sub == 0) {
       const float inv = Ls > 0.f ? 1.0f / Ls : 0.f;
       store4(P, ((int64_t)b * P.hq + (int64_t)g * G + h) * D + d4, acc * inv);
+    }
+  }
+  if (has_new && blockIdx.y == 0) {
+    // the new token into the pool (this KV head), after the outputs
+    const int64_t blk = slot / P.block_size;
+    const int off = (int)(slot % P.block_size);
+    const int chunks = D / (P.kv_dtype == PKV_F32 ? 4 : (P.kv_dtype == PKV_FP8_E4M3 ? 16 : 8));
+    if (tid < chunks) store_new_token(P, b, g, tid, blk, off, D);
+    if (g == 0 && tid == 0) {
+      // the row's table entry for the token's block and its new length
+      const int32_t L = P.lens_w[b];
+      if (L >= 0 && L / P.block_size < P.max_blocks) {
+        P.tables_w[(int64_t)b * P.max_blocks + L / P.block_size] = (int32_t)blk;
+        P.lens_w[b] = L + 1;
+      }
     }
   }
 }
@@ -1632,8 +1776,31 @@ static pkv_status check_decode(const kv_pool* pool, const paged_decode_args* a) 
     return fail(PKV_E_INVAL, "shared_prefix_blocks must lie in [0, max_blocks_per_seq]");
   if (a->shared_prefix_blocks > 0 && a->sliding_window > 0)
     return fail(PKV_E_UNSUPPORTED, "a shared prefix with a sliding window is not supported");
+  if (a->new_k) {
+    const bool same = a->new_dtype == d.kv_dtype;
+    const bool quant = d.kv_dtype == PKV_FP8_E4M3 &&
+                       (a->new_dtype == PKV_F32 || a->new_dtype == PKV_F16 || a->new_dtype == PKV_BF16);
+    if (!same && !quant) return fail(PKV_E_DTYPE, "new_dtype must be the pool's dtype (or f32/f16/bf16 into FP8)");
+    if (a->batch > 0 && (!a->new_v || !a->new_slots))
+      return fail(PKV_E_INVAL, "a fused append needs new_k, new_v and new_slots");
+    if ((reinterpret_cast<uintptr_t>(a->new_k) | reinterpret_cast<uintptr_t>(a->new_v)) % 16)
+      return fail(PKV_E_INVAL, "new_k and new_v must be 16-byte aligned");
+    if (a->batch > 0 && !a->block_tables)
+      return fail(PKV_E_INVAL, "a fused append needs block_tables");
+  } else if (a->new_v || a->new_slots) {
+    return fail(PKV_E_INVAL, "new_v / new_slots given without new_k");
+  }
   return PKV_OK;
 }
+
+// One pass per (KV head, sequence) with no merge: no shared prefix and a
+// split count of 1 (or empty tables).
+static bool single_pass(const paged_decode_args* a) {
+  return a->shared_prefix_blocks == 0 && (a->num_splits == 1 || a->max_blocks_per_seq == 0);
+}
+
+// Every pair leaves a partial for the merge: with a shared prefix or a fused append.
+static bool all_partial(const paged_decode_args* a) { return a->shared_prefix_blocks > 0 || a->new_k; }
 
 static int tokens_per_subtile(int kv) {
   return kv == PKV_F32 ? SubTile<KV_F32>::TT : (kv == PKV_FP8_E4M3 ? SubTile<KV_FP8>::TT : SubTile<KV_BF16>::TT);
@@ -1662,11 +1829,12 @@ static int64_t num_waves_for(const paged_decode_args* a, int cus) {
 }
 
 
-// Workspace: merge jobs [Hkv][B] int4, partial outputs [W][2][G][D] fp32
-// and partial (max, sum) [W][2][G][2] fp32 (range mode only), then the
-// shared-prefix partials [chunks + 1][B * Hq][D + 4] fp32 (with a shared
-// prefix; the last slot holds the own part of pairs that one wavefront held
-// whole), each part 256-byte aligned.
+// Workspace: merge jobs [Hkv][B] int4 (range mode, or every pair leaving a
+// partial), partial outputs [W][2][G][D] fp32 and partial (max, sum)
+// [W][2][G][2] fp32 (range mode), then, when every pair leaves a partial, the
+// shared-prefix partials [chunks + 1][B * Hq][D + 4] fp32 (no chunks without
+// a shared prefix; the last slot holds the own part of pairs that one
+// wavefront held whole), each part 256-byte aligned.
 struct WsLayout {
   size_t job_off, o_off, ml_off, pre_off, total;
 };
@@ -1678,13 +1846,14 @@ static WsLayout workspace_layout(const kv_pool* pool, const paged_decode_args* a
   WsLayout l;
   l.job_off = l.o_off = l.ml_off = 0;
   size_t end = 0;
+  if (!single || all_partial(a)) end = up((size_t)pool->desc.num_kv_heads * a->batch * sizeof(int4));
   if (!single) {
-    l.o_off = up((size_t)pool->desc.num_kv_heads * a->batch * sizeof(int4));
+    l.o_off = end;
     l.ml_off = l.o_off + up((size_t)W * 2 * G * pool->desc.head_dim * sizeof(float));
     end = l.ml_off + up((size_t)W * 2 * G * 2 * sizeof(float));
   }
   l.pre_off = end;
-  if (a->shared_prefix_blocks > 0)
+  if (all_partial(a))
     end += up((size_t)(pre_chunks + 1) * a->batch * a->num_q_heads * (pool->desc.head_dim + 4) * sizeof(float));
   l.total = end;
   return l;
@@ -1741,7 +1910,7 @@ static decode_fn pick_prefix(int kv, int d, int bs) {
 
 // Workspace bytes of a decode call (arguments already checked).
 static pkv_status workspace_bytes_for(const kv_pool* pool, const paged_decode_args* a, size_t* bytes_out) {
-  const bool single = a->shared_prefix_blocks == 0 && (a->num_splits == 1 || a->max_blocks_per_seq == 0);
+  const bool single = single_pass(a);
   int cus = 0;
   if ((!single && a->num_splits <= 1) || a->shared_prefix_blocks > 0) {
     const pkv_status st = device_cus(&cus);
@@ -2010,12 +2179,37 @@ static pkv_status decode_launch(const kv_pool* pool, const paged_decode_args* a,
   P.shared = a->shared_prefix_blocks;
   P.pre_chunks = 0;
   P.pre_rtiles = 0;
+  P.allpart = all_partial(a) ? 1 : 0;
+  P.fused = a->new_k ? 1 : 0;
+  P.new_src = a->new_dtype;
+  P.kv_dtype = d.kv_dtype;
+  P.block_size = d.block_size;
+  P.new_k = (const uint8_t*)a->new_k;
+  P.new_v = (const uint8_t*)a->new_v;
+  P.new_slots = a->new_slots;
+  P.k_inv = d.k_inv_scale;
+  P.v_inv = d.v_inv_scale;
+  P.tables_w = a->block_tables;
+  P.lens_w = a->context_lens;
+  if (P.fused) {
+    // the slots may be in page-locked host memory (the host block manager's
+    // buffer): the merge then reads them through its device address
+    const size_t sb = (size_t)a->batch * sizeof(int64_t);
+    if (in_one_allocation(a->new_slots, sb, hipMemoryTypeHost)) {
+      hipPointerAttribute_t at;
+      const hipError_t e = hipPointerGetAttributes(&at, a->new_slots);
+      if (e != hipSuccess || !at.devicePointer) return hip_fail(e, "hipPointerGetAttributes");
+      P.new_slots = static_cast<const int64_t*>(at.devicePointer);
+    } else if (!in_one_allocation(a->new_slots, sb, hipMemoryTypeDevice)) {
+      return fail(PKV_E_INVAL, "new_slots must lie in one device or page-locked host allocation of [batch]");
+    }
+  }
   decode_fn fn = pick_decode(d.kv_dtype, d.head_dim, d.block_size);
   if (!fn) return fail(PKV_E_UNSUPPORTED, "no kernel for this shape");
   hipStream_t s = (hipStream_t)stream;
   const int64_t segs = (int64_t)d.num_kv_heads * a->batch;
   // a shared prefix always runs in range mode (its merge joins the prefix)
-  const bool single = P.shared == 0 && (a->num_splits == 1 || a->max_blocks_per_seq == 0);
+  const bool single = single_pass(a);
 
   int cus = 0;
   if ((!single && a->num_splits <= 1) || P.shared > 0) {
@@ -2035,8 +2229,8 @@ static pkv_status decode_launch(const kv_pool* pool, const paged_decode_args* a,
   // the first kernel launched records ev[0]
   hipEvent_t ev_first = ev ? ev[0] : nullptr;
   hipError_t e;
+  if (P.allpart) P.ws_pre = reinterpret_cast<float*>(ws + wl.pre_off);
   if (P.shared > 0) {
-    P.ws_pre = reinterpret_cast<float*>(ws + wl.pre_off);
     decode_fn pfn = pick_prefix(d.kv_dtype, d.head_dim, d.block_size);
     if (!pfn) return fail(PKV_E_UNSUPPORTED, "no kernel for this shape");
     const int64_t tasks = (int64_t)d.num_kv_heads * P.pre_rtiles * P.pre_chunks;
@@ -2046,13 +2240,20 @@ static pkv_status decode_launch(const kv_pool* pool, const paged_decode_args* a,
     ev_first = nullptr;
   }
 
+  const decode_fn mfn = d.head_dim == 64 ? merge_kernel<64> : merge_kernel<128>;
   if (single) {
     P.single = 1;
     P.num_waves = 0;
+    if (P.allpart) P.ws_job = reinterpret_cast<int4*>(ws + wl.job_off);
     const int64_t grid = (segs + 3) / 4;
     e = launch(fn, dim3((uint32_t)grid), 0, s, ev_first, ev ? ev[1] : nullptr, P);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     if (nk) *nk = 1;
+    if (!P.fused) return PKV_OK;
+    // the fused append's merge: every pair's own partial and the new token
+    e = launch(mfn, dim3((uint32_t)segs, 1), 0, s, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, P);
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+    if (nk) *nk = 2;
     return PKV_OK;
   }
 
@@ -2080,8 +2281,7 @@ static pkv_status decode_launch(const kv_pool* pool, const paged_decode_args* a,
   const int np = (int)(P.group * (d.head_dim / 4));
   int pg = 1;
   while (segs * pg < 512 && np / (pg * 2) >= 16) pg *= 2;
-  e = launch(d.head_dim == 64 ? merge_kernel<64> : merge_kernel<128>, dim3((uint32_t)segs, pg), 0, s,
-             ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, P);
+  e = launch(mfn, dim3((uint32_t)segs, pg), 0, s, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, P);
   if (e != hipSuccess) return hip_fail(e, "merge launch");
   if (nk) *nk = 2;
   return PKV_OK;
