@@ -3,11 +3,14 @@
 One step is one pass of the whole decode hot path over one batch:
   1. host: reserve one slot per sequence (block_table_append_batch: on-demand
      blocks, copy-on-write of shared partial blocks),
-  2. paged_kv_append_step: the new token's K/V into its slot, and the row's
-     table entry and length into the device-resident tables (forked
-     families, whose tables change every step, instead export and upload
-     the step's metadata, copy the copy-on-write blocks and append),
-  3. paged_attention_decode (range-split decode + log-sum-exp merge).
+  2. paged_attention_decode with the fused append: the range-split decode of
+     the cached tokens, then the log-sum-exp merge, which folds in the new
+     token and writes it into its slot, the row's table entry and length
+     (device-resident tables; the slots are read from the page-locked buffer
+     the host wrote them to).  Forked families, whose tables change every
+     step, first export and upload the step's metadata and copy the
+     copy-on-write blocks.  --unfused runs paged_kv_append_step (or
+     paged_kv_append) before a plain decode instead.
 Inputs (the cache and every step's q, k, v) are resident in HBM before the
 timed region starts.  Several independently placed copies of the cache are
 rotated so the working set is several times the 256 MB Infinity Cache.
@@ -312,9 +315,15 @@ def run(args):
     shared0 = 0
     if w.lengths_kind == "prefix" and not args.no_shared_prefix:
         shared0 = w.prefix_len // w.block_size
+    # the decode call appends the step's token itself (fused append) unless
+    # --unfused asks for the separate append kernel
+    fused = not args.unfused
+    fuse_kw = lambda t, slots: (dict(new_k=steps[t][0], new_v=steps[t][1], new_dtype=w.src_dtype,
+                                     new_slots=slots) if fused else {})
     args0 = P.make_decode_args(0, B, w.num_q_heads, reps[0].max_blocks, steps[0][2], w.q_dtype,
                                reps[0].d_tables, reps[0].d_lens, scale, out, "f32",
-                               sliding_window=w.window, num_splits=args.splits, shared_prefix_blocks=shared0)
+                               sliding_window=w.window, num_splits=args.splits, shared_prefix_blocks=shared0,
+                               **fuse_kw(0, reps[0].d_slots))
     ws_bytes = P.paged_attention_workspace_size(reps[0].pool.handle, args0)
     ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
     # pinned staging ring for the per-step metadata; a buffer is rewritten only
@@ -339,14 +348,18 @@ def run(args):
         uniq = logical - kv_logical + float(np.mean([unique_kv_bytes(w, L) for L in lens_list]))
         return logical, uniq
 
-    # per-step decode arguments and timing events, made before the timed loop
+    resident = not prefix and not args.full_metadata
+    # per-step decode arguments and timing events, made before the timed loop;
+    # with the fused append a resident batch's slots are read from the
+    # page-locked staging buffer, otherwise from the uploaded metadata
     dec_args = []
     for t in range(n_total):
         rep = reps[t % len(reps)]
+        slots_src = ring[t % RING][0] if resident else rep.d_slots
         dec_args.append(P.make_decode_args(0, B, w.num_q_heads, mb, steps[t][2], w.q_dtype, rep.d_tables,
                                            rep.d_lens, scale, out, "f32", sliding_window=w.window,
                                            num_splits=args.splits, workspace=ws, workspace_bytes=ws_bytes,
-                                           shared_prefix_blocks=shared0))
+                                           shared_prefix_blocks=shared0, **fuse_kw(t, slots_src)))
     # Every TIME_EVERY-th step's decode is timed by its own kernels (attention
     # start/end, merge start/end), with events that skip the system-scope
     # fence (see HipEvent); an event still costs a little, so only a sample
@@ -360,10 +373,9 @@ def run(args):
     n_kernels = {}
     step_lens = {}
     # A steady batch keeps its tables resident on the device: one full export
-    # and upload here, then paged_kv_append_step updates them with each token.
-    # The forked branches of the prefix workload change every step and are
-    # exported and uploaded every step.
-    resident = not prefix and not args.full_metadata
+    # and upload here, then each step's call (or paged_kv_append_step, unfused)
+    # updates them with its token.  The forked branches of the prefix workload
+    # change every step and are exported and uploaded every step.
     if resident:
         buf, npb = ring[0]
         for rep in reps:
@@ -398,11 +410,14 @@ def run(args):
         if resident:
             if len(cows):
                 raise RuntimeError("copy-on-write in a batch without forks")
-            # new K/V and the rows' tables and lengths in one kernel; the
-            # slots are read from the page-locked buffer
-            P.paged_kv_append_step(h, 0, kd, vd, w.src_dtype, buf, B, rep.d_tables, rep.d_lens, mb, sptr)
+            if not fused:
+                # new K/V and the rows' tables and lengths in one kernel; the
+                # slots are read from the page-locked buffer
+                P.paged_kv_append_step(h, 0, kd, vd, w.src_dtype, buf, B, rep.d_tables, rep.d_lens, mb, sptr)
         else:
             P.block_table_export(h, seqs, mb, tables_out=tables_np, lens_out=lens_np)
+            if fused:
+                lens_np -= 1        # the cached tokens before the step's token, which the call adds
         if shared0:
             # the blocks the batch holds in common, read once by the decode
             k = P.block_table_common_prefix(h, seqs)
@@ -413,7 +428,8 @@ def run(args):
             P.kv_metadata_upload(rep.meta, buf, meta_bytes, sptr)
             if len(cows):
                 P.kv_pool_copy_blocks(h, rep.d_cows, len(cows), sptr)
-            P.paged_kv_append(h, 0, kd, vd, w.src_dtype, rep.d_slots, B, sptr)
+            if not fused:
+                P.paged_kv_append(h, 0, kd, vd, w.src_dtype, rep.d_slots, B, sptr)
         if t in sampled:
             n_kernels[t] = P.paged_attention_decode_timed(h, dec_args[t], [e.address for e in sampled[t]], sptr)
         else:
@@ -451,11 +467,17 @@ def run(args):
         last_t[t % len(reps)] = t
     order = [last_t[r] for r in sorted(last_t)]
     n_b2b = max(len(order), 20)
+    # plain decodes of the final state (a fused call would append again)
+    b2b_args = {t: P.make_decode_args(0, B, w.num_q_heads, mb, steps[t][2], w.q_dtype, reps[t % len(reps)].d_tables,
+                                      reps[t % len(reps)].d_lens, scale, out, "f32", sliding_window=w.window,
+                                      num_splits=args.splits, workspace=ws, workspace_bytes=ws_bytes,
+                                      shared_prefix_blocks=dec_args[t].shared_prefix_blocks)
+                for t in order}
     b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     b0.record(stream)
     for k in range(n_b2b):
         t = order[k % len(order)]
-        P.paged_attention_decode(reps[t % len(reps)].pool.handle, dec_args[t], sptr)
+        P.paged_attention_decode(reps[t % len(reps)].pool.handle, b2b_args[t], sptr)
     b1.record(stream)
     torch.cuda.synchronize()
     b2b_ms = b0.elapsed_time(b1) / n_b2b
@@ -529,8 +551,9 @@ def run(args):
             "head_dim": w.head_dim, "block_size": w.block_size, "kv_dtype": w.kv_dtype,
             "mean_context": float(np.mean(d.lengths)), "sliding_window": w.window,
             "num_splits": args.splits, "replicas": len(reps), "shared_prefix_blocks": shared0,
-            "metadata": ("device-resident tables updated by paged_kv_append_step" if resident
-                         else "tables exported and uploaded every step"),
+            "metadata": ("device-resident tables" if resident else "tables exported and uploaded every step"),
+            "append": ("fused: the decode call appends the step's token, its table entry and length" if fused
+                       else "separate append kernel before the decode"),
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "seq_heads_per_s": round(B * w.num_q_heads / (step_ms * 1e-3), 1),
@@ -713,6 +736,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--full-metadata", action="store_true",
                     help="export and upload every step's tables instead of keeping them resident")
+    ap.add_argument("--unfused", action="store_true",
+                    help="append the step's token with its own kernel before the decode call")
     ap.add_argument("--no-shared-prefix", action="store_true",
                     help="decode forked families without reading their common prefix once")
     ap.add_argument("--traffic", type=float, default=None,

@@ -377,9 +377,9 @@ typedef struct {
    *    does), block_tables[b][L / block_size] = new_slots[b] / block_size
    *    and context_lens[b] = L + 1, after every read of them.
    * new_slots[b] is the slot block_table_append gave (its copy-on-write
-   * pairs copied first); a slot outside the pool means row b has no new
-   * token (nothing written, L tokens attended).  L / block_size must be below
-   * max_blocks_per_seq, else the table entry and length are not written.
+   * pairs copied first).  Every row's new token is attended; a slot outside
+   * the pool, or L / block_size not below max_blocks_per_seq, leaves the
+   * token unstored and the row's table entry and length as they were.
    * Same result as paged_kv_append followed by paged_attention_decode. */
   const void* new_k;            /* device [B][Hkv][head_dim], 16-byte aligned */
   const void* new_v;            /* device [B][Hkv][head_dim], 16-byte aligned */

@@ -331,7 +331,7 @@ struct DecodeParams {
   // L + 1); merge_kernel folds in the new token as one more partial (scores
   // from new_k, values from new_v, quantised like the pool for FP8), writes
   // it into the pool at new_slots[b], writes the row's table entry and
-  // lens[b] = L + 1.  A row whose slot is outside the pool has no new token.
+  // lens[b] = L + 1.  A slot outside the pool is attended but not stored.
   int32_t fused;
   int32_t new_src;         // dtype of new_k / new_v
   int32_t kv_dtype;        // the pool's
@@ -343,6 +343,8 @@ struct DecodeParams {
   const float* v_inv;
   int32_t* tables_w;       // the same tables and lengths, written by merge_kernel
   int32_t* lens_w;
+  int32_t merge_pg;        // merge workgroups per (KV head, sequence)
+  int32_t append_spg;      // fused append: sequences per append workgroup
 };
 
 // Which piece an LDS staging slot of the decode holds (48 bytes, so that
@@ -1472,69 +1474,166 @@ __device__ __forceinline__ void store_new_token(const DecodeParams& P, int b, in
 #undef PKV_STORE
 }
 
-// Log-sum-exp merge of the pieces of a split (KV head, sequence).  Workgroup
-// (seg, y) of 256 threads owns a contiguous share of the G * D/4 output
-// positions (head h, 4 dims) of sequence-head seg; TPP threads share a
-// position, thread sub taking pieces sub, sub + TPP, ...  Each thread loads
-// the (max, sum) and o of up to 8 of its pieces at once, so the partials are
-// read in one round trip after the job; more pieces are folded in batches of
-// 8 with the usual rescaling.  The thread maxima are combined by lane
-// exchanges, then the rescaled sums by a butterfly that leaves the same bits
-// in every lane of a position (deterministic).  Piece p of a job whose first
-// piece is in range w0 is in slot (w0, first) for p = 0 and (w0 + p, 0) after.
+// Sequences whose new tokens one append workgroup of merge_kernel writes: as
+// many as give its 256 threads one token chunk (16 bytes of K and its V
+// elements) each -- every thread's loads then go out in one round trip --
+// and at most 16, whose slots are read with one coalesced load.
+static int append_seqs_per_group(int hkv, int d, int kv_dtype) {
+  const int chunks = d / (kv_dtype == PKV_F32 ? 4 : (kv_dtype == PKV_FP8_E4M3 ? 16 : 8));
+  return std::max(1, std::min(16, 256 / (hkv * chunks)));
+}
+
+// Fused append, workgroup a of the append part: the new tokens of sequences
+// a * spg .. a * spg + spg - 1 (spg = P.append_spg) into the pool (every KV
+// head), then each row's table entry and length.  A slot outside the pool is
+// not written.
+template <int D>
+__device__ void append_group(const DecodeParams& P, int a) {
+  __shared__ int64_t sl[16];
+  const int tid = threadIdx.x;
+  const int b0 = a * P.append_spg;
+  const int nb = min(P.append_spg, P.batch - b0);
+  if (tid < nb) sl[tid] = __hip_atomic_load(P.new_slots + b0 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  __syncthreads();
+  const int chunks = D / (P.kv_dtype == PKV_F32 ? 4 : (P.kv_dtype == PKV_FP8_E4M3 ? 16 : 8));
+  const int per = P.hkv * chunks;
+  const int64_t cap = P.num_blocks * P.block_size;
+  for (int t = tid; t < nb * per; t += blockDim.x) {
+    const int i = t / per;
+    const int64_t slot = sl[i];
+    if (slot < 0 || slot >= cap) continue;
+    store_new_token(P, b0 + i, (t / chunks) % P.hkv, t % chunks, slot / P.block_size,
+                    (int)(slot % P.block_size), D);
+  }
+  if (tid < nb) {
+    const int64_t slot = sl[tid];
+    const int b = b0 + tid;
+    const int32_t L = P.lens_w[b];
+    if (slot >= 0 && slot < cap && L >= 0 && L / P.block_size < P.max_blocks) {
+      // the row's table entry for the token's block and its new length
+      P.tables_w[(int64_t)b * P.max_blocks + L / P.block_size] = (int32_t)(slot / P.block_size);
+      P.lens_w[b] = L + 1;
+    }
+  }
+}
+
+// Elements lane, lane + 64, ... of a row of D (run-time dtype), as fp32,
+// all loads issued together.
+template <int D>
+__device__ __forceinline__ void load_row(int dt, const uint8_t* p, int64_t row, int lane, float (&v)[D / 64]) {
+  if (dt == PKV_F32) {
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) v[e] = src_to_f32<KV_F32>(p, row + lane + 64 * e);
+  } else if (dt == PKV_F16) {
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) v[e] = src_to_f32<KV_F16>(p, row + lane + 64 * e);
+  } else {
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) v[e] = src_to_f32<KV_BF16>(p, row + lane + 64 * e);
+  }
+}
+
+// Log-sum-exp merge of the pieces of a split (KV head, sequence).  Merge
+// workgroup x < segs * pg is (seg, y) = (x / pg, x % pg); it owns a contiguous share
+// of the G * D/4 output positions (head h, 4 dims) of sequence-head seg; TPP
+// threads share a position, thread sub taking pieces sub, sub + TPP, ...
+// Each thread loads the (max, sum) and o of up to 8 of its pieces at once,
+// so the partials are read in one round trip after the job; more pieces are
+// folded in batches of 8 with the usual rescaling.  The thread maxima are
+// combined by lane exchanges, then the rescaled sums by a butterfly that
+// leaves the same bits in every lane of a position (deterministic).  Piece p
+// of a job whose first piece is in range w0 is in slot (w0, first) for p = 0
+// and (w0 + p, 0) after.
 //
 // With a fused append the new token is one more partial of every (sequence,
 // head): o = its V row, max = its score, sum = 1.  Its scores are computed
-// first (one wavefront per head, lanes over the dims), then folded in by the
-// first thread of each position; the token is written into the pool (K, V
-// of this KV head) and, by one workgroup per sequence, into the row's table
-// entry and length, after the outputs.
+// first (one wavefront per head, lanes over the dims; the job is loaded
+// before, so both round trips overlap) and folded in by the first thread of
+// each position.  Separate workgroups write the new tokens into the
+// pool, the tables and the lengths (append_group, the first workgroups of
+// the grid); no merge workgroup reads a slot.
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeParams P) {
   constexpr int NPC = 8;   // pieces per thread per batch
-  const int64_t seg = blockIdx.x;
+  // fused append: the append workgroups come first, so that their slot reads
+  // (page-locked host memory, the longest chain of the kernel) start first
+  const int64_t nappend = P.fused ? (P.batch + P.append_spg - 1) / P.append_spg : 0;
+  if ((int64_t)blockIdx.x < nappend) {
+    append_group<D>(P, (int)blockIdx.x);
+    return;
+  }
+  const int64_t x = blockIdx.x - nappend;
+  const int64_t seg = x / P.merge_pg;
+  const int yb = (int)(x % P.merge_pg);
   const int b = (int)(seg % P.batch), g = (int)(seg / P.batch);
   const int G = P.group;
   const int tid = threadIdx.x;
+  const int4 job = P.ws_job[seg];
   __shared__ float s_new[16];          // log2-domain score of the new token, per head of the group
-  __shared__ int64_t slot_sh;
-  int64_t slot = -1;
   if (P.fused) {
     const int lane = tid & 63, wv = tid >> 6;
-    if (tid == 0) slot_sh = __hip_atomic_load(P.new_slots + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     const int qdt = P.kv_dtype == PKV_FP8_E4M3 ? PKV_BF16 : P.kv_dtype;
     const int64_t s0 = ((int64_t)P.layer * P.hkv + g) * D;   // channel scales of (layer, KV head)
-    const int64_t krow = ((int64_t)b * P.hkv + g) * D;
-    for (int h = wv; h < G; h += 4) {
-      const int64_t qrow = ((int64_t)b * P.hq + (int64_t)g * G + h) * D;
+    float k[D / 64];
+    load_row<D>(P.new_src, P.new_k, ((int64_t)b * P.hkv + g) * D, lane, k);
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) k[e] = pool_value(P, k[e], P.k_inv, P.k_scale, s0 + lane + 64 * e);
+    // heads wv, wv + 4, ... of the group: every query row's loads first, in
+    // one round trip (at most 4 heads per wavefront: G <= 16)
+    float q[4][D / 64];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (wv + 4 * u < G) load_row<D>(qdt, P.q, ((int64_t)b * P.hq + (int64_t)g * G + wv + 4 * u) * D, lane, q[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (wv + 4 * u >= G) break;
       float acc = 0.f;
-      for (int d = lane; d < D; d += 64) {
-        const float k = pool_value(P, new_src_value(P.new_src, P.new_k, krow + d), P.k_inv, P.k_scale, s0 + d);
-        acc += new_src_value(qdt, P.q, qrow + d) * k;
-      }
+#pragma unroll
+      for (int e = 0; e < D / 64; ++e) acc += q[u][e] * k[e];
       for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-      if (lane == 0) s_new[h] = acc * P.scale_log2;
+      if (lane == 0) s_new[wv + 4 * u] = acc * P.scale_log2;
     }
-    __syncthreads();
-    slot = slot_sh;
+    // the barrier that publishes s_new comes after the partials' loads (below)
   }
-  const bool has_new = P.fused && slot >= 0 && slot < P.num_blocks * P.block_size;
-  const int4 job = P.ws_job[seg];
   const int npieces = job.y;
   if (npieces == 0 && !P.allpart) return;
   const int64_t w0 = job.x;
   const int first_which = job.z;
   constexpr int D4 = D / 4;
   const int NP = G * D4;
-  const int npg = (NP + gridDim.y - 1) / gridDim.y;
-  const int pos0 = blockIdx.y * npg;
+  const int npg = (NP + P.merge_pg - 1) / P.merge_pg;
+  const int pos0 = yb * npg;
   const int pos1 = min(NP, pos0 + npg);
   int tpp = 1;
   while (tpp * 2 * npg <= 256 && tpp < 64) tpp *= 2;   // threads per position (lanes of one wavefront)
   const int sub = tid % tpp;
-  for (int pos = pos0 + tid / tpp; pos < pos1; pos += 256 / tpp) {
+  // a trip count uniform over the workgroup (a fused append has a barrier in
+  // the first trip); threads past pos1 only take part in it
+  const int per_trip = 256 / tpp;
+  const int trips = (pos1 - pos0 + per_trip - 1) / per_trip;
+  for (int trip = 0; trip < trips; ++trip) {
+    const int pos_raw = pos0 + tid / tpp + trip * per_trip;
+    const bool active = pos_raw < pos1;
+    const int pos = active ? pos_raw : pos0;
     const int h = pos / D4;
     const int d4 = (pos % D4) * 4;
+    // the new token's V elements of this position, loaded first
+    f32x4 vn = {0.f, 0.f, 0.f, 0.f};
+    if (P.fused && sub == 0) {
+      const int64_t s0 = ((int64_t)P.layer * P.hkv + g) * D;
+      const int64_t e0 = ((int64_t)b * P.hkv + g) * D + d4;    // 4 consecutive elements, one load
+      if (P.new_src == PKV_F32) {
+        vn = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(P.new_v) + e0);
+      } else {
+        const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(P.new_v) + e0);
+        const uint32_t h16[4] = {w.x & 0xffffu, w.x >> 16, w.y & 0xffffu, w.y >> 16};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          vn[e] = P.new_src == PKV_F16 ? f16_bits_to_f32(h16[e]) : bf16_bits_to_f32(h16[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vn[e] = pool_value(P, vn[e], P.v_inv, P.v_scale, s0 + d4 + e);
+    }
     auto slot_of = [&](int pc) -> int64_t { return ((w0 + pc) * 2 + (pc == 0 ? first_which : 0)) * G + h; };
     float M = -INFINITY, Ls = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -1608,13 +1707,8 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams P) {
     }
     // the new token: one more partial (its V row, its score, sum 1), folded
     // in by one thread of the position
-    if (has_new && sub == 0) {
-      const int64_t s0 = ((int64_t)P.layer * P.hkv + g) * D;
-      const int64_t vrow = ((int64_t)b * P.hkv + g) * D;
-      f32x4 vn;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        vn[e] = pool_value(P, new_src_value(P.new_src, P.new_v, vrow + d4 + e), P.v_inv, P.v_scale, s0 + d4 + e);
+    if (P.fused && trip == 0) __syncthreads();   // s_new is written
+    if (P.fused && sub == 0) {
       const float sn = s_new[h];
       const float Mb = fmaxf(M, sn);
       const float r = __builtin_amdgcn_exp2f(M - Mb);     // M = -inf: 0
@@ -1634,24 +1728,9 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams P) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) acc[c] += __shfl_xor(acc[c], off);
     }
-    if (sub == 0) {
+    if (sub == 0 && active) {
       const float inv = Ls > 0.f ? 1.0f / Ls : 0.f;
       store4(P, ((int64_t)b * P.hq + (int64_t)g * G + h) * D + d4, acc * inv);
-    }
-  }
-  if (has_new && blockIdx.y == 0) {
-    // the new token into the pool (this KV head), after the outputs
-    const int64_t blk = slot / P.block_size;
-    const int off = (int)(slot % P.block_size);
-    const int chunks = D / (P.kv_dtype == PKV_F32 ? 4 : (P.kv_dtype == PKV_FP8_E4M3 ? 16 : 8));
-    if (tid < chunks) store_new_token(P, b, g, tid, blk, off, D);
-    if (g == 0 && tid == 0) {
-      // the row's table entry for the token's block and its new length
-      const int32_t L = P.lens_w[b];
-      if (L >= 0 && L / P.block_size < P.max_blocks) {
-        P.tables_w[(int64_t)b * P.max_blocks + L / P.block_size] = (int32_t)blk;
-        P.lens_w[b] = L + 1;
-      }
     }
   }
 }
@@ -2191,6 +2270,8 @@ static pkv_status decode_launch(const kv_pool* pool, const paged_decode_args* a,
   P.v_inv = d.v_inv_scale;
   P.tables_w = a->block_tables;
   P.lens_w = a->context_lens;
+  P.merge_pg = 1;
+  P.append_spg = append_seqs_per_group(d.num_kv_heads, d.head_dim, d.kv_dtype);
   if (P.fused) {
     // the slots may be in page-locked host memory (the host block manager's
     // buffer): the merge then reads them through its device address
@@ -2250,8 +2331,11 @@ static pkv_status decode_launch(const kv_pool* pool, const paged_decode_args* a,
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     if (nk) *nk = 1;
     if (!P.fused) return PKV_OK;
-    // the fused append's merge: every pair's own partial and the new token
-    e = launch(mfn, dim3((uint32_t)segs, 1), 0, s, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, P);
+    // the fused append's merge: every pair's own partial and the new token,
+    // and the workgroups that store the new tokens
+    P.merge_pg = 1;
+    const int64_t mgrid = segs + (a->batch + P.append_spg - 1) / P.append_spg;
+    e = launch(mfn, dim3((uint32_t)mgrid), 0, s, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, P);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
     if (nk) *nk = 2;
     return PKV_OK;
@@ -2281,7 +2365,9 @@ static pkv_status decode_launch(const kv_pool* pool, const paged_decode_args* a,
   const int np = (int)(P.group * (d.head_dim / 4));
   int pg = 1;
   while (segs * pg < 512 && np / (pg * 2) >= 16) pg *= 2;
-  e = launch(mfn, dim3((uint32_t)segs, pg), 0, s, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, P);
+  P.merge_pg = pg;
+  const int64_t mgrid = segs * pg + (P.fused ? (a->batch + P.append_spg - 1) / P.append_spg : 0);
+  e = launch(mfn, dim3((uint32_t)mgrid), 0, s, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, P);
   if (e != hipSuccess) return hip_fail(e, "merge launch");
   if (nk) *nk = 2;
   return PKV_OK;

@@ -91,7 +91,7 @@ class FusedState:
         lens_before = self.d_lens.cpu().numpy().copy()
         slot_arr = np.asarray(slots, dtype=np.int64).copy()
         if drop_row is not None:
-            slot_arr[drop_row] = -1            # this row gets no new token
+            slot_arr[drop_row] = -1            # outside the pool: attended, not stored
         d_slots = torch.from_numpy(slot_arr).pin_memory() if pinned else torch.from_numpy(slot_arr).cuda()
         out = torch.full((B, w.num_q_heads, w.head_dim), float("nan"), dtype=torch.float32, device="cuda")
         kd, vd = to_dev(kb), to_dev(vb)
@@ -106,14 +106,9 @@ class FusedState:
         torch.cuda.synchronize()
         got = out_to_f64(out, "f32")
         # oracle: the same token appended, then plain attention over L + 1
-        keep = [i for i in range(B) if i != drop_row]
-        self.opool.append(0, kb[keep], vb[keep], w.src_dtype, [oslots[i] for i in keep])
+        self.opool.append(0, kb, vb, w.src_dtype, oslots)
         otables, olens = self.bm.export(self.seqs, self.mb)
-        lens_att = olens.copy()
-        if drop_row is not None:
-            lens_att[drop_row] -= 1
-        ref = decode_attention(self.opool, 0, qb, w.q_dtype, otables, lens_att, 1.0 / math.sqrt(w.head_dim),
-                               window)
+        ref = decode_attention(self.opool, 0, qb, w.q_dtype, otables, olens, 1.0 / math.sqrt(w.head_dim), window)
         # device tables and lengths now hold the step's token
         dt, dl = self.d_tables.cpu().numpy(), self.d_lens.cpu().numpy()
         if drop_row is None:
@@ -174,7 +169,8 @@ def test_fused_append_with_window(name, window):
         st.close()
 
 
-def test_fused_append_row_without_new_token():
+def test_fused_append_slot_outside_the_pool_is_not_stored():
+    # the row's token is still attended; its table entry and length stay
     w = CASES["gqa8_bf16"]
     d = wl.draw(w, extra_blocks=w.batch * 2)
     st = FusedState(w, d)
