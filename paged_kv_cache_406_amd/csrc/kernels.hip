@@ -705,10 +705,12 @@ struct Decoder {
   }
 
   // Every lane's tokens of the sub-tile lie in a real block and in [lo, L),
-  // so nothing needs masking (the same answer in every lane).
+  // so nothing needs masking (the same answer in every lane: a scalar
+  // value, so the masked code below is branched around, not executed under
+  // an exec mask).
   static __device__ __forceinline__ bool tile_full(const VTile& T, int32_t lo, int32_t L, int kg) {
     const int32_t t0 = T.tok0 + TPG * kg;
-    return __all(T.ok && t0 >= lo && t0 + TPG <= L);
+    return uniform((int)__all(T.ok && t0 >= lo && t0 + TPG <= L)) != 0;
   }
 
   // The exponentials of a (head, piece) are taken relative to a reference
@@ -732,11 +734,16 @@ struct Decoder {
 #pragma unroll
         for (int r = 0; r < 4; ++r) s[t][r] = S[t][r] * scale_log2;
     } else {
+      // The token base goes through an empty asm statement here, so that
+      // the compares below cannot be hoisted above the branch into the
+      // full-tile path (which would then run them on every sub-tile).
+      int32_t base = T.tok0 + TPG * kg;
+      asm volatile("" : "+v"(base));
 #pragma unroll
       for (int t = 0; t < NQT; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int32_t tok = T.tok0 + TPG * kg + 4 * t + r;
+          const int32_t tok = base + 4 * t + r;
           const bool valid = T.ok && tok >= lo && tok < L;
           s[t][r] = valid ? S[t][r] * scale_log2 : -INFINITY;
         }
@@ -773,10 +780,12 @@ struct Decoder {
   static __device__ __forceinline__ void pv(VTile& T, const float (&p)[NQT][4], State& st, int32_t lo, int32_t L,
                                             int kg) {
     if (!tile_full(T, lo, L, kg)) {
+      int32_t base = T.tok0 + TPG * kg;   // kept below the branch (see softmax)
+      asm volatile("" : "+v"(base));
       uint32_t vmask[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int e = 0; e < TPG; ++e) {
-        const int32_t tok = T.tok0 + TPG * kg + e;
+        const int32_t tok = base + e;
         const bool valid = T.ok && tok >= lo && tok < L;
         const uint32_t field = EB == 4 ? 0xffffffffu : (EB == 2 ? 0xffffu : 0xffu);
         vmask[e / EPW] |= valid ? field << (8 * EB * (e % EPW)) : 0u;
@@ -1287,8 +1296,8 @@ struct Decoder {
       }
     };
 
-    // Staggered pipeline over sub-tiles: the K loads of sub-tile s+1 are in
-    // flight while s is scored, its V loads while s is accumulated.
+    // Pipeline over sub-tiles in two register buffers: the K and V loads of
+    // sub-tile s+1 are in flight while s is scored and accumulated.
     const int64_t nsub = (r1 - r0) * SPU;
     KTile K0, K1;
     VTile V0, V1;
@@ -1314,12 +1323,11 @@ struct Decoder {
       if (n1) {
         a1 = where(last1);
         load_k(K1, a1);
+        load_v(V1, a1);
       }
       __builtin_amdgcn_sched_barrier(0);
       qk(K0, q, S);
       softmax(V0, S, st, p, cs.lo, cs.L, P.scale_log2, kg);
-      __builtin_amdgcn_sched_barrier(0);
-      if (n1) load_v(V1, a1);
       __builtin_amdgcn_sched_barrier(0);
       pv(V0, p, st, cs.lo, cs.L, kg);
       __builtin_amdgcn_sched_barrier(0);
@@ -1329,12 +1337,11 @@ struct Decoder {
       if (n2) {
         a0 = where(last0);
         load_k(K0, a0);
+        load_v(V0, a0);
       }
       __builtin_amdgcn_sched_barrier(0);
       qk(K1, q, S);
       softmax(V1, S, st, p, cs.lo, cs.L, P.scale_log2, kg);
-      __builtin_amdgcn_sched_barrier(0);
-      if (n2) load_v(V0, a0);
       __builtin_amdgcn_sched_barrier(0);
       pv(V1, p, st, cs.lo, cs.L, kg);
       __builtin_amdgcn_sched_barrier(0);
