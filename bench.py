@@ -67,13 +67,13 @@ WORKLOAD_NAMES = {
 # kernel source it was measured on (kernels_sha()); for any other source the
 # figure is not reported.
 MEASURED_TRAFFIC = {
-    "c3": (506.3e6, "0326ddf5dcb9303b"),
-    "c2": (1977.1e6, "0326ddf5dcb9303b"),
-    "c2_bs128": (2027.5e6, "0326ddf5dcb9303b"),
-    "c5": (2154.2e6, "0326ddf5dcb9303b"),
-    "c5_fp8": (1081.7e6, "0326ddf5dcb9303b"),
-    "c5w": (72.3e6, "0326ddf5dcb9303b"),
-    "c4": (379.7e6, "0326ddf5dcb9303b"),   # the whole call: prefix, suffix and merge kernels
+    "c3": (507.0e6, "6c4469231ea0c88c"),
+    "c2": (1981.3e6, "6c4469231ea0c88c"),
+    "c2_bs128": (2039.3e6, "6c4469231ea0c88c"),
+    "c5": (2158.5e6, "6c4469231ea0c88c"),
+    "c5_fp8": (1080.5e6, "6c4469231ea0c88c"),
+    "c5w": (72.3e6, "6c4469231ea0c88c"),
+    "c4": (383.6e6, "6c4469231ea0c88c"),   # the whole call: prefix, suffix and merge kernels
 }
 
 
