@@ -224,3 +224,55 @@ def test_full_size_prefix_shared_step():
         assert P.kv_pool_free_list(h) == st.bm.free_list()
     finally:
         st.close()
+
+
+@pytest.mark.parametrize("name", ["c3", "c5_fp8", "c2"])
+def test_full_size_fused_append_step(name):
+    # the call bench.py times: device-resident tables and lengths, the host
+    # reserves one slot per sequence, and one paged_attention_decode appends
+    # the step's token (fused) and attends it; every output row against the
+    # oracle, the device tables and lengths bit for bit, and the new tokens'
+    # pool bytes
+    w = wl.WORKLOADS[name]
+    d = wl.draw(w, extra_blocks=w.batch)
+    st = FullState(w, d)
+    h = st.pool.handle
+    try:
+        mb = max(len(st.bm.table(o)) for o in st.oseqs) + 1
+        t0, l0 = P.block_table_export(h, st.seqs, mb)
+        d_tables, d_lens = torch.from_numpy(t0).cuda(), torch.from_numpy(l0).cuda()
+        slots, cows = P.block_table_append_batch(h, st.seqs)
+        oslots, ocows = st.bm.append_batch(st.oseqs)
+        assert slots.tolist() == oslots and len(ocows) == 0
+        kb, vb, qb = wl.step_tokens_bits(w, 0)
+        pinned = torch.from_numpy(np.asarray(slots, np.int64).copy()).pin_memory()
+        out = torch.full((w.batch, w.num_q_heads, w.head_dim), float("nan"), dtype=torch.float32, device="cuda")
+        a = P.make_decode_args(0, w.batch, w.num_q_heads, mb, to_dev(qb), w.q_dtype, d_tables, d_lens,
+                               1.0 / math.sqrt(w.head_dim), out, "f32", sliding_window=w.window,
+                               new_k=to_dev(kb), new_v=to_dev(vb), new_dtype=w.src_dtype, new_slots=pinned)
+        nbytes = P.paged_attention_workspace_size(h, a)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        a.workspace, a.workspace_bytes = ws.data_ptr(), nbytes
+        a._refs = a._refs + (ws,)
+        P.paged_attention_decode(h, a)
+        torch.cuda.synchronize()
+        st.opool.append(0, kb, vb, w.src_dtype, oslots)
+        otables, olens = st.bm.export(st.oseqs, mb)
+        assert np.array_equal(d_tables.cpu().numpy(), otables) and np.array_equal(d_lens.cpu().numpy(), olens)
+        err = st.check(out_to_f64(out, "f32"), st.reference(qb, otables, olens))
+        # the new tokens' K/V bytes in the pool (one token per sequence)
+        eb = wl.ELEM_BYTES[w.kv_dtype]
+        npd = {4: np.uint32, 2: np.uint16, 1: np.uint8}[eb]
+        x = 16 // eb
+        NB, H, BS, D = d.num_blocks, w.num_kv_heads, w.block_size, w.head_dim
+        k = st.pool.k_cache.cpu().numpy().view(npd).reshape(NB, H, D // x, BS, x)
+        blk, off = np.divmod(np.asarray(oslots), BS)
+        got_k = k[blk, :, :, off, :].reshape(len(oslots), H, D)
+        assert np.array_equal(got_k, st.opool.k[0, blk, :, off])
+        vt = min(BS, {"f32": 16, "f16": 32, "bf16": 32, "fp8": 64}[w.kv_dtype])
+        v = st.pool.v_cache.cpu().numpy().view(npd).reshape(NB, H, BS // vt, D, vt)
+        got_v = v[blk, :, off // vt, :, off % vt]
+        assert np.array_equal(got_v, st.opool.v[0, blk, :, off])
+        print(f"[full-size] {name} fused step: max|gpu - oracle| = {err:.3e}")
+    finally:
+        st.close()
