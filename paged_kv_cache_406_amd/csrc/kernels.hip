@@ -166,20 +166,74 @@ struct AppendParams {
   int32_t max_blocks;
 };
 
-// One token's K group c (X channels, 16 bytes in the pool) and its X V
-// elements (dims e * D/X + c) of KV head h, from source row `row` (element
-// index of the token's head row in k / v), into block blk at offset off of
-// `layer`.
+// Raw bits of source element idx (fp32, or fp16 / bf16 in the low half).
+template <int SRC>
+__device__ __forceinline__ uint32_t src_bits(const uint8_t* p, int64_t idx) {
+  if constexpr (SRC == KV_F32) return reinterpret_cast<const uint32_t*>(p)[idx];
+  else return reinterpret_cast<const uint16_t*>(p)[idx];
+}
+template <int SRC>
+__device__ __forceinline__ float bits_to_f32(uint32_t b) {
+  if constexpr (SRC == KV_F32) return __uint_as_float(b);
+  else if constexpr (SRC == KV_F16) return f16_bits_to_f32(b);
+  else return bf16_bits_to_f32(b);
+}
+
+// What one thread stores of a token: its K group c (X channels, 16 bytes in
+// the pool) and its X V elements (dims e * D/X + c) of one KV head, as raw
+// source bits, with the channels' inverse scales for FP8.  Loading it is
+// split from storing it so that every load is issued before the first
+// store (the compiler may not move a load above a store that could alias
+// it, so loads and stores taken in turn would cost one memory round trip
+// per element), and before the slot is known.
 template <int KV, int SRC>
-__device__ __forceinline__ void store_token_chunk(uint8_t* kc, uint8_t* vc, const uint8_t* k, const uint8_t* v,
-                                                  const float* k_inv, const float* v_inv, int64_t num_blocks,
-                                                  int hkv, int d, int bs, int layer, int64_t row, int c, int h,
-                                                  int64_t blk, int off) {
+struct TokenChunk {
+  static constexpr int X = 16 / Elem<KV>::bytes;
+  u32x4 k;                 // same dtype: the K group's bits
+  uint32_t v[X];           // same dtype: the V elements' bits
+  uint32_t kb[X], vb[X];   // FP8: source bits of the K channels and V elements
+  float ki[X], vi[X];      // FP8: their inverse scales
+};
+
+// The loads of chunk c of KV head h from source row `row` (element index of
+// the token's head row in k / v) of `layer`.
+template <int KV, int SRC>
+__device__ __forceinline__ TokenChunk<KV, SRC> load_token_chunk(const uint8_t* k, const uint8_t* v,
+                                                                const float* k_inv, const float* v_inv, int hkv,
+                                                                int d, int layer, int64_t row, int c, int h) {
+  constexpr int X = TokenChunk<KV, SRC>::X;
+  const int chunks = d / X;
+  TokenChunk<KV, SRC> t;
+  if constexpr (KV == SRC) {
+    t.k = *reinterpret_cast<const u32x4*>(k + (row + (int64_t)c * X) * Elem<KV>::bytes);
+#pragma unroll
+    for (int e = 0; e < X; ++e) t.v[e] = src_bits<SRC>(v, row + (int64_t)e * chunks + c);
+  } else {
+    static_assert(KV == KV_FP8, "only same-dtype copy or FP8 quantisation");
+    const int64_t s0 = ((int64_t)layer * hkv + h) * d;   // channel scales of (layer, head)
+#pragma unroll
+    for (int e = 0; e < X; ++e) {
+      const int kd = c * X + e;
+      const int64_t vd = (int64_t)e * chunks + c;
+      t.kb[e] = src_bits<SRC>(k, row + kd);
+      t.ki[e] = k_inv[s0 + kd];
+      t.vb[e] = src_bits<SRC>(v, row + vd);
+      t.vi[e] = v_inv[s0 + vd];
+    }
+  }
+  return t;
+}
+
+// Store a loaded chunk into block blk at offset off of `layer`: a bit copy,
+// or the E4M3 codes of x * inv_scale.
+template <int KV, int SRC>
+__device__ __forceinline__ void store_token_chunk(const TokenChunk<KV, SRC>& t, uint8_t* kc, uint8_t* vc,
+                                                  int64_t num_blocks, int hkv, int d, int bs, int layer, int c,
+                                                  int h, int64_t blk, int off) {
   constexpr int EB = Elem<KV>::bytes;
-  constexpr int X = 16 / EB;
+  constexpr int X = TokenChunk<KV, SRC>::X;
   const int chunks = d / X;
   const int64_t tile = ((int64_t)layer * num_blocks + blk) * hkv + h;
-  const int64_t src0 = row + (int64_t)c * X;       // this thread's K chunk
   uint8_t* kdst = kc + ((tile * (d / X) + c) * bs + off) * 16;
   // V runs of vt tokens, channel-major inside a run: element dim of this
   // token sits vt elements after element dim - 1.  The thread's e-th V
@@ -188,33 +242,25 @@ __device__ __forceinline__ void store_token_chunk(uint8_t* kc, uint8_t* vc, cons
   // by one instruction.
   const int vt = v_run(bs, SubTile<KV>::TT);
   uint8_t* vdst = vc + (tile * d * bs + (int64_t)(off / vt) * d * vt + off % vt) * EB;
+  // non-temporal stores: the cache lines this token touches (one 16-byte K
+  // group, D V elements in bs-element rows) are not read again by this kernel
   if constexpr (KV == SRC) {
-    // non-temporal stores: the cache lines this token touches (one 16-byte
-    // K group, D two- or four-byte V elements in bs-element rows) are not
-    // read again by this kernel
-    const u32x4 kv = *reinterpret_cast<const u32x4*>(k + src0 * EB);
-    __builtin_nontemporal_store(kv, reinterpret_cast<u32x4*>(kdst));
+    __builtin_nontemporal_store(t.k, reinterpret_cast<u32x4*>(kdst));
 #pragma unroll
     for (int e = 0; e < X; ++e) {
-      const int64_t dim = (int64_t)e * chunks + c;
-      uint8_t* dst = vdst + dim * vt * EB;
+      uint8_t* dst = vdst + ((int64_t)e * chunks + c) * vt * EB;
       if constexpr (EB == 4)
-        __builtin_nontemporal_store(reinterpret_cast<const uint32_t*>(v)[row + dim], reinterpret_cast<uint32_t*>(dst));
-      else if constexpr (EB == 2)
-        __builtin_nontemporal_store(reinterpret_cast<const uint16_t*>(v)[row + dim], reinterpret_cast<uint16_t*>(dst));
+        __builtin_nontemporal_store(t.v[e], reinterpret_cast<uint32_t*>(dst));
+      else
+        __builtin_nontemporal_store((uint16_t)t.v[e], reinterpret_cast<uint16_t*>(dst));
     }
   } else {
-    static_assert(KV == KV_FP8, "only same-dtype copy or FP8 quantisation");
-    const int64_t s0 = ((int64_t)layer * hkv + h) * d;   // channel scales of (layer, head)
     uint32_t kw[4] = {0, 0, 0, 0};
 #pragma unroll
     for (int e = 0; e < X; ++e) {
-      const int kd = c * X + e;
-      const float kx = src_to_f32<SRC>(k, row + kd) * k_inv[s0 + kd];
-      kw[e >> 2] |= f32_to_e4m3(kx) << (8 * (e & 3));
-      const int64_t vd = (int64_t)e * chunks + c;
-      const float vx = src_to_f32<SRC>(v, row + vd) * v_inv[s0 + vd];
-      __builtin_nontemporal_store((uint8_t)f32_to_e4m3(vx), vdst + vd * vt);
+      kw[e >> 2] |= f32_to_e4m3(bits_to_f32<SRC>(t.kb[e]) * t.ki[e]) << (8 * (e & 3));
+      __builtin_nontemporal_store((uint8_t)f32_to_e4m3(bits_to_f32<SRC>(t.vb[e]) * t.vi[e]),
+                                  vdst + ((int64_t)e * chunks + c) * vt);
     }
     __builtin_nontemporal_store(u32x4{kw[0], kw[1], kw[2], kw[3]}, reinterpret_cast<u32x4*>(kdst));
   }
@@ -238,6 +284,13 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams P) {
   const int lane = (int)(threadIdx.x & 63);
   const int64_t pos = t - i * per_row;
   const int src = pos <= lane ? lane - (int)pos : 0;
+  // this thread's chunk, loaded before its slot is known (lanes past the end
+  // load the last chunk, so that no branch sits around the loads)
+  const int64_t tl = t < total ? t : total - 1;
+  const int hl = (int)((tl / chunks) % P.hkv);
+  const TokenChunk<KV, SRC> tok = load_token_chunk<KV, SRC>(P.k, P.v, P.k_inv, P.v_inv, P.hkv, P.d, P.layer,
+                                                            ((tl / per_row) * P.hkv + hl) * P.d,
+                                                            (int)(tl % chunks), hl);
   int64_t slot = -1;
   if (t < total && lane == src)
     slot = P.tables ? __hip_atomic_load(P.slots + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) : P.slots[i];
@@ -255,9 +308,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams P) {
       P.lens[i] = pos + 1;
     }
   }
-  const int64_t row = (i * P.hkv + h) * P.d;       // element index of the token's (head) row
-  store_token_chunk<KV, SRC>(P.kc, P.vc, P.k, P.v, P.k_inv, P.v_inv, P.num_blocks, P.hkv, P.d, P.bs, P.layer,
-                             row, c, h, blk, off);
+  store_token_chunk<KV, SRC>(tok, P.kc, P.vc, P.num_blocks, P.hkv, P.d, P.bs, P.layer, c, h, blk, off);
 }
 
 // ---------------------------------------------------------------------------
@@ -1441,44 +1492,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   Dec::prefix_group(P, g, (int)(rem / P.pre_chunks), (int)(rem % P.pre_chunks), stage);
 }
 
-// Source element idx of new_k / new_v as fp32 (run-time source dtype).
-__device__ __forceinline__ float new_src_value(int src, const uint8_t* p, int64_t idx) {
-  if (src == PKV_F32) return src_to_f32<KV_F32>(p, idx);
-  if (src == PKV_F16) return src_to_f32<KV_F16>(p, idx);
-  return src_to_f32<KV_BF16>(p, idx);
-}
-
-// The value the pool holds for source element x of channel (layer, head)
-// offset s: x itself, or (FP8) the E4M3 code of x * inv_scale decoded and
-// times the scale -- what the decode reads back.
-__device__ __forceinline__ float pool_value(const DecodeParams& P, float x, const float* inv, const float* scale,
-                                            int64_t s) {
-  if (P.kv_dtype != PKV_FP8_E4M3) return x;
-  const uint32_t code = f32_to_e4m3(x * inv[s]);
-  const bf16x2 w = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(code, 1.0f, false);
-  return (float)w[0] * scale[s];
-}
-
-// Fused append: write the new token's 16-byte K group c and its V elements
-// of KV head h into the pool (run-time pool and source dtypes).
-__device__ __forceinline__ void store_new_token(const DecodeParams& P, int b, int h, int c, int64_t blk, int off,
-                                                int D) {
-  uint8_t* kc = const_cast<uint8_t*>(P.kc);
-  uint8_t* vc = const_cast<uint8_t*>(P.vc);
-  const int64_t row = ((int64_t)b * P.hkv + h) * D;
-#define PKV_STORE(KVT, SRCT)                                                                               \
-  store_token_chunk<KVT, SRCT>(kc, vc, P.new_k, P.new_v, P.k_inv, P.v_inv, P.num_blocks, P.hkv, D,          \
-                               P.block_size, P.layer, row, c, h, blk, off)
-  switch (P.kv_dtype) {
-    case PKV_F32: PKV_STORE(KV_F32, KV_F32); break;
-    case PKV_F16: PKV_STORE(KV_F16, KV_F16); break;
-    case PKV_BF16: PKV_STORE(KV_BF16, KV_BF16); break;
-    default:
-      if (P.new_src == PKV_F32) PKV_STORE(KV_FP8, KV_F32);
-      else if (P.new_src == PKV_F16) PKV_STORE(KV_FP8, KV_F16);
-      else PKV_STORE(KV_FP8, KV_BF16);
+// The value the pool holds for a source value x of one channel: x itself,
+// or (FP8) the E4M3 code of x * inv decoded and times the channel's scale --
+// what the decode reads back.
+template <int KV>
+__device__ __forceinline__ float pool_value(float x, float inv, float scale) {
+  if constexpr (KV != KV_FP8) {
+    return x;
+  } else {
+    const uint32_t code = f32_to_e4m3(x * inv);
+    const bf16x2 w = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(code, 1.0f, false);
+    return (float)w[0] * scale;
   }
-#undef PKV_STORE
 }
 
 // Sequences whose new tokens one append workgroup of merge_kernel writes: as
@@ -1492,52 +1517,62 @@ static int append_seqs_per_group(int hkv, int d, int kv_dtype) {
 
 // Fused append, workgroup a of the append part: the new tokens of sequences
 // a * spg .. a * spg + spg - 1 (spg = P.append_spg) into the pool (every KV
-// head), then each row's table entry and length.  A slot outside the pool is
-// not written.
-template <int D>
+// head), and each row's table entry and length.  A slot outside the pool is
+// not written.  The tokens' loads go out with the slot reads, and a row's
+// table entry and length are written as soon as its slot is known: no
+// memory round trip waits for another that it does not depend on.
+template <int D, int KV, int SRC>
 __device__ void append_group(const DecodeParams& P, int a) {
   __shared__ int64_t sl[16];
   const int tid = threadIdx.x;
   const int b0 = a * P.append_spg;
   const int nb = min(P.append_spg, P.batch - b0);
-  if (tid < nb) sl[tid] = __hip_atomic_load(P.new_slots + b0 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-  __syncthreads();
-  const int chunks = D / (P.kv_dtype == PKV_F32 ? 4 : (P.kv_dtype == PKV_FP8_E4M3 ? 16 : 8));
-  const int per = P.hkv * chunks;
   const int64_t cap = P.num_blocks * P.block_size;
-  for (int t = tid; t < nb * per; t += blockDim.x) {
-    const int i = t / per;
-    const int64_t slot = sl[i];
-    if (slot < 0 || slot >= cap) continue;
-    store_new_token(P, b0 + i, (t / chunks) % P.hkv, t % chunks, slot / P.block_size,
-                    (int)(slot % P.block_size), D);
-  }
+  constexpr int chunks = D / (16 / Elem<KV>::bytes);
+  const int per = P.hkv * chunks;
+  const int total = nb * per;
+  uint8_t* kc = const_cast<uint8_t*>(P.kc);
+  uint8_t* vc = const_cast<uint8_t*>(P.vc);
+  // this thread's first chunk, loaded with the slots (threads past the end
+  // load the last chunk, so that no branch sits around the loads)
+  const int t0 = min(tid, total - 1);
+  const int h0 = (t0 / chunks) % P.hkv;
+  const TokenChunk<KV, SRC> first = load_token_chunk<KV, SRC>(
+      P.new_k, P.new_v, P.k_inv, P.v_inv, P.hkv, D, P.layer, ((int64_t)(b0 + t0 / per) * P.hkv + h0) * D,
+      t0 % chunks, h0);
   if (tid < nb) {
-    const int64_t slot = sl[tid];
     const int b = b0 + tid;
     const int32_t L = P.lens_w[b];
-    if (slot >= 0 && slot < cap && L >= 0 && L / P.block_size < P.max_blocks) {
+    const int64_t slot = __hip_atomic_load(P.new_slots + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    // no short-circuit: the length's load must not wait behind the slot's
+    const bool ok = (slot >= 0) & (slot < cap) & (L >= 0) & (L / P.block_size < P.max_blocks);
+    sl[tid] = slot;
+    if (ok) {
       // the row's table entry for the token's block and its new length
       P.tables_w[(int64_t)b * P.max_blocks + L / P.block_size] = (int32_t)(slot / P.block_size);
       P.lens_w[b] = L + 1;
     }
   }
+  __syncthreads();
+  for (int t = tid; t < total; t += blockDim.x) {
+    const int i = t / per;
+    const int64_t slot = sl[i];
+    if (slot < 0 || slot >= cap) continue;
+    const int h = (t / chunks) % P.hkv;
+    const TokenChunk<KV, SRC> tok =
+        t == tid ? first
+                 : load_token_chunk<KV, SRC>(P.new_k, P.new_v, P.k_inv, P.v_inv, P.hkv, D, P.layer,
+                                             ((int64_t)(b0 + i) * P.hkv + h) * D, t % chunks, h);
+    store_token_chunk<KV, SRC>(tok, kc, vc, P.num_blocks, P.hkv, D, P.block_size, P.layer, t % chunks, h,
+                               slot / P.block_size, (int)(slot % P.block_size));
+  }
 }
 
-// Elements lane, lane + 64, ... of a row of D (run-time dtype), as fp32,
-// all loads issued together.
-template <int D>
-__device__ __forceinline__ void load_row(int dt, const uint8_t* p, int64_t row, int lane, float (&v)[D / 64]) {
-  if (dt == PKV_F32) {
+// Elements lane, lane + 64, ... of a row of D (element type T), as fp32.
+template <int D, int T>
+__device__ __forceinline__ void load_row(const uint8_t* p, int64_t row, int lane, float (&v)[D / 64]) {
 #pragma unroll
-    for (int e = 0; e < D / 64; ++e) v[e] = src_to_f32<KV_F32>(p, row + lane + 64 * e);
-  } else if (dt == PKV_F16) {
-#pragma unroll
-    for (int e = 0; e < D / 64; ++e) v[e] = src_to_f32<KV_F16>(p, row + lane + 64 * e);
-  } else {
-#pragma unroll
-    for (int e = 0; e < D / 64; ++e) v[e] = src_to_f32<KV_BF16>(p, row + lane + 64 * e);
-  }
+  for (int e = 0; e < D / 64; ++e) v[e] = src_to_f32<T>(p, row + lane + 64 * e);
 }
 
 // Log-sum-exp merge of the pieces of a split (KV head, sequence).  Merge
@@ -1552,22 +1587,32 @@ __device__ __forceinline__ void load_row(int dt, const uint8_t* p, int64_t row, 
 // of a job whose first piece is in range w0 is in slot (w0, first) for p = 0
 // and (w0 + p, 0) after.
 //
-// With a fused append the new token is one more partial of every (sequence,
-// head): o = its V row, max = its score, sum = 1.  Its scores are computed
-// first (one wavefront per head, lanes over the dims; the job is loaded
-// before, so both round trips overlap) and folded in by the first thread of
-// each position.  Separate workgroups write the new tokens into the
-// pool, the tables and the lengths (append_group, the first workgroups of
-// the grid); no merge workgroup reads a slot.
-template <int D>
+// With a fused append (NKV >= 0: pool dtype NKV, source dtype NSRC) the new
+// token is one more partial of every (sequence, head): o = its V row, max =
+// its score, sum = 1.  Its K elements, channel scales and the query rows
+// are loaded with the job, its V elements before the partials; its scores
+// (one wavefront per head, lanes over the dims) are computed after the
+// partials' loads have gone out, and the first thread of each position
+// folds it in.  The dtypes are compile-time constants so that these loads
+// are straight-line code and go out together.  Separate workgroups write
+// the new tokens into the pool, the tables and the lengths (append_group,
+// the first workgroups of the grid); no merge workgroup reads a slot.
+template <int D, int NKV, int NSRC>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeParams P) {
   constexpr int NPC = 8;   // pieces per thread per batch
+  constexpr bool FUSED = NKV >= 0;
+  constexpr int KV = FUSED ? NKV : KV_F32;
+  constexpr int SRC = FUSED ? NSRC : KV_F32;
+  constexpr int QT = KV == KV_FP8 ? KV_BF16 : KV;   // the queries' dtype
   // fused append: the append workgroups come first, so that their slot reads
   // (page-locked host memory, the longest chain of the kernel) start first
-  const int64_t nappend = P.fused ? (P.batch + P.append_spg - 1) / P.append_spg : 0;
-  if ((int64_t)blockIdx.x < nappend) {
-    append_group<D>(P, (int)blockIdx.x);
-    return;
+  int64_t nappend = 0;
+  if constexpr (FUSED) {
+    nappend = (P.batch + P.append_spg - 1) / P.append_spg;
+    if ((int64_t)blockIdx.x < nappend) {
+      append_group<D, KV, SRC>(P, (int)blockIdx.x);
+      return;
+    }
   }
   const int64_t x = blockIdx.x - nappend;
   const int64_t seg = x / P.merge_pg;
@@ -1575,35 +1620,31 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams P) {
   const int b = (int)(seg % P.batch), g = (int)(seg / P.batch);
   const int G = P.group;
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
   const int4 job = P.ws_job[seg];
   __shared__ float s_new[16];          // log2-domain score of the new token, per head of the group
-  if (P.fused) {
-    const int lane = tid & 63, wv = tid >> 6;
-    const int qdt = P.kv_dtype == PKV_FP8_E4M3 ? PKV_BF16 : P.kv_dtype;
-    const int64_t s0 = ((int64_t)P.layer * P.hkv + g) * D;   // channel scales of (layer, KV head)
-    float k[D / 64];
-    load_row<D>(P.new_src, P.new_k, ((int64_t)b * P.hkv + g) * D, lane, k);
+  const int64_t s0 = ((int64_t)P.layer * P.hkv + g) * D;   // channel scales of (layer, KV head)
+  // fused append: the new token's K elements lane, lane + 64, ... (with their
+  // channel scales) and the query rows of heads wv, wv + 4, ... of the group
+  // (at most 4 per wavefront: G <= 16)
+  float kx[D / 64], ki[D / 64], ks[D / 64], q[4][D / 64];
+  if constexpr (FUSED) {
+    load_row<D, SRC>(P.new_k, ((int64_t)b * P.hkv + g) * D, lane, kx);
+    if constexpr (KV == KV_FP8) {
 #pragma unroll
-    for (int e = 0; e < D / 64; ++e) k[e] = pool_value(P, k[e], P.k_inv, P.k_scale, s0 + lane + 64 * e);
-    // heads wv, wv + 4, ... of the group: every query row's loads first, in
-    // one round trip (at most 4 heads per wavefront: G <= 16)
-    float q[4][D / 64];
+      for (int e = 0; e < D / 64; ++e) {
+        ki[e] = P.k_inv[s0 + lane + 64 * e];
+        ks[e] = P.k_scale[s0 + lane + 64 * e];
+      }
+    }
+    // rows past the group repeat its last head (never used): no branch
+    // around a load, so that every load goes out before the first wait
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      if (wv + 4 * u < G) load_row<D>(qdt, P.q, ((int64_t)b * P.hq + (int64_t)g * G + wv + 4 * u) * D, lane, q[u]);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (wv + 4 * u >= G) break;
-      float acc = 0.f;
-#pragma unroll
-      for (int e = 0; e < D / 64; ++e) acc += q[u][e] * k[e];
-      for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-      if (lane == 0) s_new[wv + 4 * u] = acc * P.scale_log2;
-    }
-    // the barrier that publishes s_new comes after the partials' loads (below)
+      load_row<D, QT>(P.q, ((int64_t)b * P.hq + (int64_t)g * G + min(wv + 4 * u, G - 1)) * D, lane, q[u]);
   }
   const int npieces = job.y;
-  if (npieces == 0 && !P.allpart) return;
+  if (!FUSED && npieces == 0 && !P.allpart) return;
   const int64_t w0 = job.x;
   const int first_which = job.z;
   constexpr int D4 = D / 4;
@@ -1624,22 +1665,26 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams P) {
     const int pos = active ? pos_raw : pos0;
     const int h = pos / D4;
     const int d4 = (pos % D4) * 4;
-    // the new token's V elements of this position, loaded first
-    f32x4 vn = {0.f, 0.f, 0.f, 0.f};
-    if (P.fused && sub == 0) {
-      const int64_t s0 = ((int64_t)P.layer * P.hkv + g) * D;
-      const int64_t e0 = ((int64_t)b * P.hkv + g) * D + d4;    // 4 consecutive elements, one load
-      if (P.new_src == PKV_F32) {
-        vn = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(P.new_v) + e0);
-      } else {
-        const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(P.new_v) + e0);
-        const uint32_t h16[4] = {w.x & 0xffffu, w.x >> 16, w.y & 0xffffu, w.y >> 16};
+    // the new token's V elements of this position (and their channel
+    // scales), loaded before the partials and converted after them
+    f32x4 vraw = {0.f, 0.f, 0.f, 0.f};
+    uint2 vbits = {0u, 0u};
+    float vi[4], vs[4];
+    if constexpr (FUSED) {
+      if (sub == 0) {
+        const int64_t e0 = ((int64_t)b * P.hkv + g) * D + d4;    // 4 consecutive elements, one load
+        if constexpr (SRC == KV_F32)
+          vraw = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(P.new_v) + e0);
+        else
+          vbits = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(P.new_v) + e0);
+        if constexpr (KV == KV_FP8) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          vn[e] = P.new_src == PKV_F16 ? f16_bits_to_f32(h16[e]) : bf16_bits_to_f32(h16[e]);
+          for (int e = 0; e < 4; ++e) {
+            vi[e] = P.v_inv[s0 + d4 + e];
+            vs[e] = P.v_scale[s0 + d4 + e];
+          }
+        }
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) vn[e] = pool_value(P, vn[e], P.v_inv, P.v_scale, s0 + d4 + e);
     }
     auto slot_of = [&](int pc) -> int64_t { return ((w0 + pc) * 2 + (pc == 0 ? first_which : 0)) * G + h; };
     float M = -INFINITY, Ls = 0.f;
@@ -1714,15 +1759,49 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams P) {
     }
     // the new token: one more partial (its V row, its score, sum 1), folded
     // in by one thread of the position
-    if (P.fused && trip == 0) __syncthreads();   // s_new is written
-    if (P.fused && sub == 0) {
-      const float sn = s_new[h];
-      const float Mb = fmaxf(M, sn);
-      const float r = __builtin_amdgcn_exp2f(M - Mb);     // M = -inf: 0
-      const float wt = __builtin_amdgcn_exp2f(sn - Mb);
-      acc = acc * r + vn * wt;
-      Ls = Ls * r + wt;
-      M = Mb;
+    if constexpr (FUSED) {
+      if (trip == 0) {
+        // its scores, heads wv, wv + 4, ... on wavefront wv: the four sums
+        // are reduced together, so that their lane exchanges overlap
+        float kv[D / 64];
+#pragma unroll
+        for (int e = 0; e < D / 64; ++e) kv[e] = pool_value<KV>(kx[e], ki[e], ks[e]);
+        float dot[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          dot[u] = 0.f;
+#pragma unroll
+          for (int e = 0; e < D / 64; ++e) dot[u] += q[u][e] * kv[e];
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) dot[u] += __shfl_xor(dot[u], off);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (lane == 0 && wv + 4 * u < G) s_new[wv + 4 * u] = dot[u] * P.scale_log2;
+        __syncthreads();
+      }
+      if (sub == 0) {
+        f32x4 vn;
+        if constexpr (SRC == KV_F32) {
+          vn = vraw;
+        } else {
+          const uint32_t h16[4] = {vbits.x & 0xffffu, vbits.x >> 16, vbits.y & 0xffffu, vbits.y >> 16};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vn[e] = SRC == KV_F16 ? f16_bits_to_f32(h16[e]) : bf16_bits_to_f32(h16[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vn[e] = pool_value<KV>(vn[e], vi[e], vs[e]);
+        const float sn = s_new[h];
+        const float Mb = fmaxf(M, sn);
+        const float r = __builtin_amdgcn_exp2f(M - Mb);     // M = -inf: 0
+        const float wt = __builtin_amdgcn_exp2f(sn - Mb);
+        acc = acc * r + vn * wt;
+        Ls = Ls * r + wt;
+        M = Mb;
+      }
     }
     // combine the tpp threads of the position: common max, rescale, sum
     float Mall = M;
@@ -1971,6 +2050,21 @@ static decode_fn pick_decode(int kv, int d, int bs) {
     case PKV_FP8_E4M3: return pick_decode_d<KV_FP8>(d, bs);
   }
   return nullptr;
+}
+
+// The merge, compiled per (pool dtype, new-token dtype) for a fused append.
+template <int D>
+static decode_fn pick_merge(const DecodeParams& P) {
+  if (!P.fused) return merge_kernel<D, -1, -1>;
+  switch (P.kv_dtype) {
+    case PKV_F32: return merge_kernel<D, KV_F32, KV_F32>;
+    case PKV_F16: return merge_kernel<D, KV_F16, KV_F16>;
+    case PKV_BF16: return merge_kernel<D, KV_BF16, KV_BF16>;
+    default:
+      if (P.new_src == PKV_F32) return merge_kernel<D, KV_FP8, KV_F32>;
+      if (P.new_src == PKV_F16) return merge_kernel<D, KV_FP8, KV_F16>;
+      return merge_kernel<D, KV_FP8, KV_BF16>;
+  }
 }
 
 template <int KV, int D>
@@ -2328,7 +2422,7 @@ static pkv_status decode_launch(const kv_pool* pool, const paged_decode_args* a,
     ev_first = nullptr;
   }
 
-  const decode_fn mfn = d.head_dim == 64 ? merge_kernel<64> : merge_kernel<128>;
+  const decode_fn mfn = d.head_dim == 64 ? pick_merge<64>(P) : pick_merge<128>(P);
   if (single) {
     P.single = 1;
     P.num_waves = 0;
