@@ -377,9 +377,11 @@ typedef struct {
    *    does), block_tables[b][L / block_size] = new_slots[b] / block_size
    *    and context_lens[b] = L + 1, after every read of them.
    * new_slots[b] is the slot block_table_append gave (its copy-on-write
-   * pairs copied first).  Every row's new token is attended; a slot outside
-   * the pool, or L / block_size not below max_blocks_per_seq, leaves the
-   * token unstored and the row's table entry and length as they were.
+   * pairs copied first).  Every row's new token is attended.  A slot
+   * outside the pool leaves the token unstored; such a slot, or
+   * L / block_size not below max_blocks_per_seq, leaves the row's table
+   * entry and length as they were.  The slots are read on the device while
+   * the call runs.
    * Same result as paged_kv_append followed by paged_attention_decode. */
   const void* new_k;            /* device [B][Hkv][head_dim], 16-byte aligned */
   const void* new_v;            /* device [B][Hkv][head_dim], 16-byte aligned */

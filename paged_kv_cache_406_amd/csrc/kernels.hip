@@ -1518,9 +1518,8 @@ static int append_seqs_per_group(int hkv, int d, int kv_dtype) {
 // Fused append, workgroup a of the append part: the new tokens of sequences
 // a * spg .. a * spg + spg - 1 (spg = P.append_spg) into the pool (every KV
 // head), and each row's table entry and length.  A slot outside the pool is
-// not written.  The tokens' loads go out with the slot reads, and a row's
-// table entry and length are written as soon as its slot is known: no
-// memory round trip waits for another that it does not depend on.
+// not written.  The slots are read first, with one load per sequence; every
+// thread then loads its token chunk whole and stores it.
 template <int D, int KV, int SRC>
 __device__ void append_group(const DecodeParams& P, int a) {
   __shared__ int64_t sl[16];
@@ -1528,41 +1527,32 @@ __device__ void append_group(const DecodeParams& P, int a) {
   const int b0 = a * P.append_spg;
   const int nb = min(P.append_spg, P.batch - b0);
   const int64_t cap = P.num_blocks * P.block_size;
-  constexpr int chunks = D / (16 / Elem<KV>::bytes);
-  const int per = P.hkv * chunks;
-  const int total = nb * per;
-  uint8_t* kc = const_cast<uint8_t*>(P.kc);
-  uint8_t* vc = const_cast<uint8_t*>(P.vc);
-  // this thread's first chunk, loaded with the slots (threads past the end
-  // load the last chunk, so that no branch sits around the loads)
-  const int t0 = min(tid, total - 1);
-  const int h0 = (t0 / chunks) % P.hkv;
-  const TokenChunk<KV, SRC> first = load_token_chunk<KV, SRC>(
-      P.new_k, P.new_v, P.k_inv, P.v_inv, P.hkv, D, P.layer, ((int64_t)(b0 + t0 / per) * P.hkv + h0) * D,
-      t0 % chunks, h0);
   if (tid < nb) {
     const int b = b0 + tid;
-    const int32_t L = P.lens_w[b];
     const int64_t slot = __hip_atomic_load(P.new_slots + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    // no short-circuit: the length's load must not wait behind the slot's
-    const bool ok = (slot >= 0) & (slot < cap) & (L >= 0) & (L / P.block_size < P.max_blocks);
     sl[tid] = slot;
-    if (ok) {
-      // the row's table entry for the token's block and its new length
-      P.tables_w[(int64_t)b * P.max_blocks + L / P.block_size] = (int32_t)(slot / P.block_size);
-      P.lens_w[b] = L + 1;
+    if (slot >= 0 && slot < cap) {
+      const int32_t L = P.lens_w[b];
+      if (L >= 0 && L / P.block_size < P.max_blocks) {
+        // the row's table entry for the token's block and its new length
+        P.tables_w[(int64_t)b * P.max_blocks + L / P.block_size] = (int32_t)(slot / P.block_size);
+        P.lens_w[b] = L + 1;
+      }
     }
   }
   __syncthreads();
-  for (int t = tid; t < total; t += blockDim.x) {
+  constexpr int chunks = D / (16 / Elem<KV>::bytes);
+  const int per = P.hkv * chunks;
+  uint8_t* kc = const_cast<uint8_t*>(P.kc);
+  uint8_t* vc = const_cast<uint8_t*>(P.vc);
+  for (int t = tid; t < nb * per; t += blockDim.x) {
     const int i = t / per;
     const int64_t slot = sl[i];
     if (slot < 0 || slot >= cap) continue;
     const int h = (t / chunks) % P.hkv;
-    const TokenChunk<KV, SRC> tok =
-        t == tid ? first
-                 : load_token_chunk<KV, SRC>(P.new_k, P.new_v, P.k_inv, P.v_inv, P.hkv, D, P.layer,
-                                             ((int64_t)(b0 + i) * P.hkv + h) * D, t % chunks, h);
+    const TokenChunk<KV, SRC> tok = load_token_chunk<KV, SRC>(P.new_k, P.new_v, P.k_inv, P.v_inv, P.hkv, D,
+                                                              P.layer, ((int64_t)(b0 + i) * P.hkv + h) * D,
+                                                              t % chunks, h);
     store_token_chunk<KV, SRC>(tok, kc, vc, P.num_blocks, P.hkv, D, P.block_size, P.layer, t % chunks, h,
                                slot / P.block_size, (int)(slot % P.block_size));
   }

@@ -181,6 +181,45 @@ def test_fused_append_slot_outside_the_pool_is_not_stored():
         st.close()
 
 
+def test_fused_append_row_without_table_room():
+    # row 0's token starts a third block, but the tables are two entries wide:
+    # the token is attended and stored at its slot; the row's table entry and
+    # length stay as they were; the other rows step as usual
+    w = wl.scaled(wl.WORKLOADS["c3"], batch=4, num_q_heads=8, num_kv_heads=2, lengths_kind="fixed",
+                  lengths_args=(32, 5, 31, 17))
+    d = wl.draw(w, extra_blocks=8)
+    st = FusedState(w, d)
+    h = st.pool.handle
+    try:
+        mb, B = 2, w.batch
+        t0, l0 = P.block_table_export(h, st.seqs, mb)
+        d_tables, d_lens = torch.from_numpy(t0.copy()).cuda(), torch.from_numpy(l0.copy()).cuda()
+        slots, cows = P.block_table_append_batch(h, st.seqs)
+        oslots, _ = st.bm.append_batch(st.seqs)
+        assert slots.tolist() == oslots and len(cows) == 0 and slots[0] % w.block_size == 0
+        kb, vb, qb = wl.step_tokens_bits(w, 0, B)
+        scale = 1.0 / math.sqrt(w.head_dim)
+        out = torch.full((B, w.num_q_heads, w.head_dim), float("nan"), dtype=torch.float32, device="cuda")
+        a = P.make_decode_args(0, B, w.num_q_heads, mb, to_dev(qb), w.q_dtype, d_tables, d_lens, scale, out, "f32",
+                               new_k=to_dev(kb), new_v=to_dev(vb), new_dtype=w.src_dtype,
+                               new_slots=torch.from_numpy(np.asarray(slots, np.int64)).pin_memory())
+        nbytes = P.paged_attention_workspace_size(h, a)
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+        a.workspace, a.workspace_bytes = ws.data_ptr(), nbytes
+        P.paged_attention_decode(h, a)
+        torch.cuda.synchronize()
+        st.opool.append(0, kb, vb, w.src_dtype, oslots)
+        otables, olens = st.bm.export(st.seqs, mb + 1)
+        ref = decode_attention(st.opool, 0, qb, w.q_dtype, otables, olens, scale)
+        assert np.abs(out_to_f64(out, "f32") - ref).max() <= TOL[w.kv_dtype]
+        dt, dl = d_tables.cpu().numpy(), d_lens.cpu().numpy()
+        assert dl[0] == 32 and np.array_equal(dt[0], t0[0])
+        assert np.array_equal(dl[1:], olens[1:]) and np.array_equal(dt[1:], otables[1:, :mb])
+        st.pool_bits_exact()
+    finally:
+        st.close()
+
+
 def test_fused_append_shared_prefix_branch_step():
     # forked branches of a shared prompt: copy-on-write of the partial last
     # blocks, then the fused call reading the common prefix once
