@@ -398,6 +398,16 @@ struct DecodeParams {
   int32_t append_spg;      // fused append: sequences per append workgroup
 };
 
+// Fused append, pools other than FP8: decode_kernel's workgroups past the
+// first decode_wgs store the new tokens and copy each row's slot to ws_slots
+// [B] (workspace); merge_kernel then writes the rows' table entries and
+// lengths.  A kernel argument of its own, so that DecodeParams, and the code
+// built for kernels that do not read these, stays as it is.
+struct TailParams {
+  int64_t* ws_slots;
+  int32_t decode_wgs;
+};
+
 // Which piece an LDS staging slot of the decode holds (48 bytes, so that
 // slots and wavefront areas stay 16-byte aligned).
 struct PieceTag {
@@ -1410,6 +1420,82 @@ struct Decoder {
   }
 };
 
+// Fused append, workgroup a of an append part: the new tokens of sequences
+// a * spg .. a * spg + spg - 1 (spg = P.append_spg) into the pool (every KV
+// head).  A slot outside the pool is not written.  The slots are read first,
+// one load per sequence; every thread then loads its token chunk whole and
+// stores it.
+//  - ROWS = false: workgroups after decode_kernel's own, so that they run in
+//    its tail.  Each row's slot goes to ws_slots, and merge_kernel writes the
+//    rows' table entries and lengths, which the decode reads.  The token's
+//    slot is a position of its own row past the cached tokens (a block
+//    block_table_append made the row's own by copy-on-write), which no
+//    wavefront attends as a cached token.
+//  - ROWS = true: the first workgroups of merge_kernel (FP8 pools), after
+//    the decode; they also write each row's table entry and length.
+template <int D, int KV, int SRC, bool ROWS>
+__device__ void append_group(const DecodeParams& P, const TailParams& T, int a) {
+  __shared__ int64_t sl[16];
+  const int tid = threadIdx.x;
+  const int b0 = a * P.append_spg;
+  const int nb = min(P.append_spg, P.batch - b0);
+  const int64_t cap = P.num_blocks * P.block_size;
+  if (tid < nb) {
+    const int b = b0 + tid;
+    const int64_t slot = __hip_atomic_load(P.new_slots + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    sl[tid] = slot;
+    if constexpr (ROWS) {
+      if (slot >= 0 && slot < cap) {
+        const int32_t L = P.lens_w[b];
+        if (L >= 0 && L / P.block_size < P.max_blocks) {
+          // the row's table entry for the token's block and its new length
+          P.tables_w[(int64_t)b * P.max_blocks + L / P.block_size] = (int32_t)(slot / P.block_size);
+          P.lens_w[b] = L + 1;
+        }
+      }
+    } else {
+      T.ws_slots[b] = slot;
+    }
+  }
+  __syncthreads();
+  constexpr int chunks = D / (16 / Elem<KV>::bytes);
+  const int per = P.hkv * chunks;
+  uint8_t* kc = const_cast<uint8_t*>(P.kc);
+  uint8_t* vc = const_cast<uint8_t*>(P.vc);
+  for (int t = tid; t < nb * per; t += blockDim.x) {
+    const int i = t / per;
+    const int64_t slot = sl[i];
+    if (slot < 0 || slot >= cap) continue;
+    const int h = (t / chunks) % P.hkv;
+    const TokenChunk<KV, SRC> tok = load_token_chunk<KV, SRC>(P.new_k, P.new_v, P.k_inv, P.v_inv, P.hkv, D,
+                                                              P.layer, ((int64_t)(b0 + i) * P.hkv + h) * D,
+                                                              t % chunks, h);
+    store_token_chunk<KV, SRC>(tok, kc, vc, P.num_blocks, P.hkv, D, P.block_size, P.layer, t % chunks, h,
+                               slot / P.block_size, (int)(slot % P.block_size));
+  }
+}
+
+// Workgroups at the front of the fused merge: the FP8 append groups, or
+// one per 256 rows for the rows' tables and lengths.
+__host__ __device__ inline int64_t merge_row_groups(const DecodeParams& P) {
+  return P.kv_dtype == PKV_FP8_E4M3 ? (P.batch + P.append_spg - 1) / P.append_spg : (P.batch + 255) / 256;
+}
+
+// Fused append, after the decode: rows a * 256 .. a * 256 + 255 take the
+// token's block as their table entry at L / block_size and L + 1 as their
+// length (a slot outside the pool, or no room in the table: neither).
+__device__ void update_rows(const DecodeParams& P, const TailParams& T, int a) {
+  const int b = a * 256 + (int)threadIdx.x;
+  if (b >= P.batch) return;
+  const int64_t slot = T.ws_slots[b];
+  const int32_t L = P.lens_w[b];
+  const int64_t cap = P.num_blocks * P.block_size;
+  if (slot >= 0 && slot < cap && L >= 0 && L / P.block_size < P.max_blocks) {
+    P.tables_w[(int64_t)b * P.max_blocks + L / P.block_size] = (int32_t)(slot / P.block_size);
+    P.lens_w[b] = L + 1;
+  }
+}
+
 template <int KV, int D, int BS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void decode_kernel(DecodeParams P) {
   typedef Decoder<KV, D, BS> Dec;
@@ -1476,6 +1562,92 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 }
 
+// decode_kernel's body for decode_append_kernel: the decode over the first
+// nwg workgroups of the grid.  The same steps as decode_kernel (which uses
+// the whole grid); decode_kernel keeps its own copy because its generated
+// code, the FP8 one above all, changed and slowed when it was built from a
+// shared body.
+template <int KV, int D, int BS>
+__device__ __forceinline__ void decode_body(DecodeParams P, uint32_t nwg) {
+  typedef Decoder<KV, D, BS> Dec;
+  constexpr int U = Units<KV, BS>::U;
+  extern __shared__ int32_t C[];
+  const int lane = threadIdx.x & 63;
+  const int wid = uniform((int)(threadIdx.x >> 6));  // wave-uniform: keeps all work indices scalar
+  int64_t wg = blockIdx.x;
+  if (P.xcd_remap) wg = (wg % 8) * (nwg / 8) + wg / 8;
+  const int64_t w = wg * 4 + wid;
+
+  if (P.single) {
+    // one wavefront per (KV head, sequence), KV-head major
+    if (w >= (int64_t)P.hkv * P.batch) return;
+    const int g = (int)(w / P.batch);
+    const int b = (int)(w % P.batch);
+    int32_t L, lo, first, nu;
+    seq_extent<BS, U>(P, b, &L, &lo, &first, &nu);
+    if (nu == 0) {
+      // nothing cached to attend: zeros, or (fused append) the new token
+      // alone, which merge_kernel writes
+      if (!P.allpart) write_zero_rows<D>(P, b, g, lane);
+      else if (lane == 0) P.ws_job[w] = make_int4(0, 0, 0, 0);
+      return;
+    }
+    Dec::stream(P, nullptr, 0, 0, 0, 0, 0, 0, g, b, nullptr);
+    return;
+  }
+
+  scan_units<BS, U>(P, C);
+  const int64_t t_head = C[P.batch];
+  const int64_t T = t_head * P.hkv;
+  // sequences with nothing to attend get zero rows
+  const int64_t nseg = (int64_t)P.hkv * P.batch;
+  const int64_t launched = (int64_t)nwg * 4;
+  for (int64_t seg = w; seg < nseg; seg += launched) {
+    const int b = (int)(seg % P.batch);
+    if (C[b + 1] == C[b]) {
+      // nothing of its own to attend: zeros, or (shared prefix, fused append)
+      // the merge of the prefix partials and the new token alone, written by
+      // merge_kernel
+      if (!P.allpart) write_zero_rows<D>(P, b, (int)(seg / P.batch), lane);
+      if (lane == 0) P.ws_job[seg] = make_int4(0, 0, 0, 0);
+    }
+  }
+  if (w >= P.num_waves) return;
+  // all units of all (KV head, sequence) pairs laid end to end, KV-head
+  // major, cut into W equal non-empty ranges
+  const int64_t W = P.num_waves < T ? P.num_waves : T;
+  if (w < W) {
+    const int64_t r0 = range_start(w, T, W);
+    const int64_t r1 = range_start(w + 1, T, W);
+    const int g = (int)(r0 / t_head);
+    const int32_t r = (int32_t)(r0 % t_head);
+    // largest b with C[b] <= r: the pair holding unit r0 (it has units)
+    int lo_b = 0, hi_b = P.batch - 1;
+    while (lo_b < hi_b) {
+      const int mid = (lo_b + hi_b + 1) >> 1;
+      if (C[mid] <= r) lo_b = mid;
+      else hi_b = mid - 1;
+    }
+    uint8_t* stage = reinterpret_cast<uint8_t*>(C) + P.stage_off + wid * Dec::stage_area_bytes(P.group, P.nstage);
+    Dec::stream(P, C, t_head, T, W, w, r0, r1, g, uniform(lo_b), stage);
+  }
+}
+
+// The decode of a call with a fused append (pools other than FP8): the
+// workgroups past the decode's store the new tokens in its tail.  A kernel
+// of its own so that the plain decode's code is not changed by it (the FP8
+// decode, whose scalar registers are at their limit, slowed when it held
+// this path).
+template <int KV, int D, int BS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void decode_append_kernel(
+    DecodeParams P, TailParams TP) {
+  if ((int)blockIdx.x >= TP.decode_wgs) {
+    append_group<D, KV, KV, false>(P, TP, (int)blockIdx.x - TP.decode_wgs);
+    return;
+  }
+  decode_body<KV, D, BS>(P, (uint32_t)TP.decode_wgs);
+}
+
 // Shared prefix: workgroup x takes (KV head g, row group rg, token chunk c),
 // KV-head major, so the workgroups of one head sit on one XCD and its prefix
 // blocks stay in that XCD's L2.
@@ -1515,49 +1687,6 @@ static int append_seqs_per_group(int hkv, int d, int kv_dtype) {
   return std::max(1, std::min(16, 256 / (hkv * chunks)));
 }
 
-// Fused append, workgroup a of the append part: the new tokens of sequences
-// a * spg .. a * spg + spg - 1 (spg = P.append_spg) into the pool (every KV
-// head), and each row's table entry and length.  A slot outside the pool is
-// not written.  The slots are read first, with one load per sequence; every
-// thread then loads its token chunk whole and stores it.
-template <int D, int KV, int SRC>
-__device__ void append_group(const DecodeParams& P, int a) {
-  __shared__ int64_t sl[16];
-  const int tid = threadIdx.x;
-  const int b0 = a * P.append_spg;
-  const int nb = min(P.append_spg, P.batch - b0);
-  const int64_t cap = P.num_blocks * P.block_size;
-  if (tid < nb) {
-    const int b = b0 + tid;
-    const int64_t slot = __hip_atomic_load(P.new_slots + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    sl[tid] = slot;
-    if (slot >= 0 && slot < cap) {
-      const int32_t L = P.lens_w[b];
-      if (L >= 0 && L / P.block_size < P.max_blocks) {
-        // the row's table entry for the token's block and its new length
-        P.tables_w[(int64_t)b * P.max_blocks + L / P.block_size] = (int32_t)(slot / P.block_size);
-        P.lens_w[b] = L + 1;
-      }
-    }
-  }
-  __syncthreads();
-  constexpr int chunks = D / (16 / Elem<KV>::bytes);
-  const int per = P.hkv * chunks;
-  uint8_t* kc = const_cast<uint8_t*>(P.kc);
-  uint8_t* vc = const_cast<uint8_t*>(P.vc);
-  for (int t = tid; t < nb * per; t += blockDim.x) {
-    const int i = t / per;
-    const int64_t slot = sl[i];
-    if (slot < 0 || slot >= cap) continue;
-    const int h = (t / chunks) % P.hkv;
-    const TokenChunk<KV, SRC> tok = load_token_chunk<KV, SRC>(P.new_k, P.new_v, P.k_inv, P.v_inv, P.hkv, D,
-                                                              P.layer, ((int64_t)(b0 + i) * P.hkv + h) * D,
-                                                              t % chunks, h);
-    store_token_chunk<KV, SRC>(tok, kc, vc, P.num_blocks, P.hkv, D, P.block_size, P.layer, t % chunks, h,
-                               slot / P.block_size, (int)(slot % P.block_size));
-  }
-}
-
 // Elements lane, lane + 64, ... of a row of D (element type T), as fp32.
 template <int D, int T>
 __device__ __forceinline__ void load_row(const uint8_t* p, int64_t row, int lane, float (&v)[D / 64]) {
@@ -1584,27 +1713,31 @@ __device__ __forceinline__ void load_row(const uint8_t* p, int64_t row, int lane
 // (one wavefront per head, lanes over the dims) are computed after the
 // partials' loads have gone out, and the first thread of each position
 // folds it in.  The dtypes are compile-time constants so that these loads
-// are straight-line code and go out together.  Separate workgroups write
-// the new tokens into the pool, the tables and the lengths (append_group,
-// the first workgroups of the grid); no merge workgroup reads a slot.
+// are straight-line code and go out together.  The first workgroups of this
+// grid write the rows' table entries and lengths (update_rows; the tokens
+// are already in the pool, stored in the decode's tail), or for an FP8 pool
+// store the tokens too (append_group).  Kept out of the FP8 decode, that
+// code slowed its stream loop.
 template <int D, int NKV, int NSRC>
-__global__ __launch_bounds__(256) void merge_kernel(DecodeParams P) {
+__global__ __launch_bounds__(256) void merge_kernel(DecodeParams P, TailParams TP) {
   constexpr int NPC = 8;   // pieces per thread per batch
   constexpr bool FUSED = NKV >= 0;
   constexpr int KV = FUSED ? NKV : KV_F32;
   constexpr int SRC = FUSED ? NSRC : KV_F32;
   constexpr int QT = KV == KV_FP8 ? KV_BF16 : KV;   // the queries' dtype
-  // fused append: the append workgroups come first, so that their slot reads
-  // (page-locked host memory, the longest chain of the kernel) start first
-  int64_t nappend = 0;
+  // fused append: the first workgroups write the rows' table entries and
+  // lengths (the decode, which reads them, has finished), and for an FP8
+  // pool also store the new tokens
+  int64_t nmeta = 0;
   if constexpr (FUSED) {
-    nappend = (P.batch + P.append_spg - 1) / P.append_spg;
-    if ((int64_t)blockIdx.x < nappend) {
-      append_group<D, KV, SRC>(P, (int)blockIdx.x);
+    nmeta = merge_row_groups(P);
+    if ((int64_t)blockIdx.x < nmeta) {
+      if constexpr (KV == KV_FP8) append_group<D, KV, SRC, true>(P, TP, (int)blockIdx.x);
+      else update_rows(P, TP, (int)blockIdx.x);
       return;
     }
   }
-  const int64_t x = blockIdx.x - nappend;
+  const int64_t x = blockIdx.x - nmeta;
   const int64_t seg = x / P.merge_pg;
   const int yb = (int)(x % P.merge_pg);
   const int b = (int)(seg % P.batch), g = (int)(seg / P.batch);
@@ -1989,9 +2122,10 @@ static int64_t num_waves_for(const paged_decode_args* a, int cus) {
 // [W][2][G][2] fp32 (range mode), then, when every pair leaves a partial, the
 // shared-prefix partials [chunks + 1][B * Hq][D + 4] fp32 (no chunks without
 // a shared prefix; the last slot holds the own part of pairs that one
-// wavefront held whole), each part 256-byte aligned.
+// wavefront held whole), and, with a fused append, the slots [B] int64; each
+// part 256-byte aligned.
 struct WsLayout {
-  size_t job_off, o_off, ml_off, pre_off, total;
+  size_t job_off, o_off, ml_off, pre_off, slot_off, total;
 };
 
 static WsLayout workspace_layout(const kv_pool* pool, const paged_decode_args* a, int64_t W, bool single,
@@ -2010,11 +2144,16 @@ static WsLayout workspace_layout(const kv_pool* pool, const paged_decode_args* a
   l.pre_off = end;
   if (all_partial(a))
     end += up((size_t)(pre_chunks + 1) * a->batch * a->num_q_heads * (pool->desc.head_dim + 4) * sizeof(float));
+  // fused append: the slots, as the append workgroups read them
+  l.slot_off = end;
+  if (a->new_k) end += up((size_t)a->batch * sizeof(int64_t));
   l.total = end;
   return l;
 }
 
 typedef void (*decode_fn)(DecodeParams);
+typedef void (*tail_fn)(DecodeParams, TailParams);
+typedef void (*prefix_fn)(DecodeParams);
 
 template <int KV, int D>
 static decode_fn pick_decode_bs(int bs) {
@@ -2042,9 +2181,35 @@ static decode_fn pick_decode(int kv, int d, int bs) {
   return nullptr;
 }
 
+template <int KV, int D>
+static tail_fn pick_decode_append_bs(int bs) {
+  switch (bs) {
+    case 16: return decode_append_kernel<KV, D, 16>;
+    case 32: return decode_append_kernel<KV, D, 32>;
+    case 64: return decode_append_kernel<KV, D, 64>;
+    case 128: return decode_append_kernel<KV, D, 128>;
+  }
+  return nullptr;
+}
+
+template <int KV>
+static tail_fn pick_decode_append_d(int d, int bs) {
+  return d == 64 ? pick_decode_append_bs<KV, 64>(bs) : pick_decode_append_bs<KV, 128>(bs);
+}
+
+// The decode that also stores a fused append's tokens (not for FP8 pools).
+static tail_fn pick_decode_append(int kv, int d, int bs) {
+  switch (kv) {
+    case PKV_F32: return pick_decode_append_d<KV_F32>(d, bs);
+    case PKV_F16: return pick_decode_append_d<KV_F16>(d, bs);
+    case PKV_BF16: return pick_decode_append_d<KV_BF16>(d, bs);
+  }
+  return nullptr;
+}
+
 // The merge, compiled per (pool dtype, new-token dtype) for a fused append.
 template <int D>
-static decode_fn pick_merge(const DecodeParams& P) {
+static tail_fn pick_merge(const DecodeParams& P) {
   if (!P.fused) return merge_kernel<D, -1, -1>;
   switch (P.kv_dtype) {
     case PKV_F32: return merge_kernel<D, KV_F32, KV_F32>;
@@ -2058,7 +2223,7 @@ static decode_fn pick_merge(const DecodeParams& P) {
 }
 
 template <int KV, int D>
-static decode_fn pick_prefix_bs(int bs) {
+static prefix_fn pick_prefix_bs(int bs) {
   switch (bs) {
     case 16: return prefix_kernel<KV, D, 16>;
     case 32: return prefix_kernel<KV, D, 32>;
@@ -2068,7 +2233,7 @@ static decode_fn pick_prefix_bs(int bs) {
   return nullptr;
 }
 
-static decode_fn pick_prefix(int kv, int d, int bs) {
+static prefix_fn pick_prefix(int kv, int d, int bs) {
   switch (kv) {
     case PKV_F32: return d == 64 ? pick_prefix_bs<KV_F32, 64>(bs) : pick_prefix_bs<KV_F32, 128>(bs);
     case PKV_F16: return d == 64 ? pick_prefix_bs<KV_F16, 64>(bs) : pick_prefix_bs<KV_F16, 128>(bs);
@@ -2363,6 +2528,9 @@ static pkv_status decode_launch(const kv_pool* pool, const paged_decode_args* a,
   P.lens_w = a->context_lens;
   P.merge_pg = 1;
   P.append_spg = append_seqs_per_group(d.num_kv_heads, d.head_dim, d.kv_dtype);
+  TailParams TP;
+  TP.decode_wgs = 0;
+  TP.ws_slots = nullptr;
   if (P.fused) {
     // the slots may be in page-locked host memory (the host block manager's
     // buffer): the merge then reads them through its device address
@@ -2378,6 +2546,10 @@ static pkv_status decode_launch(const kv_pool* pool, const paged_decode_args* a,
   }
   decode_fn fn = pick_decode(d.kv_dtype, d.head_dim, d.block_size);
   if (!fn) return fail(PKV_E_UNSUPPORTED, "no kernel for this shape");
+  // fused append into a pool other than FP8: the decode's tail stores the tokens
+  const tail_fn afn =
+      P.fused && d.kv_dtype != PKV_FP8_E4M3 ? pick_decode_append(d.kv_dtype, d.head_dim, d.block_size) : nullptr;
+  if (P.fused && d.kv_dtype != PKV_FP8_E4M3 && !afn) return fail(PKV_E_UNSUPPORTED, "no kernel for this shape");
   hipStream_t s = (hipStream_t)stream;
   const int64_t segs = (int64_t)d.num_kv_heads * a->batch;
   // a shared prefix always runs in range mode (its merge joins the prefix)
@@ -2402,8 +2574,13 @@ static pkv_status decode_launch(const kv_pool* pool, const paged_decode_args* a,
   hipEvent_t ev_first = ev ? ev[0] : nullptr;
   hipError_t e;
   if (P.allpart) P.ws_pre = reinterpret_cast<float*>(ws + wl.pre_off);
+  if (P.fused) TP.ws_slots = reinterpret_cast<int64_t*>(ws + wl.slot_off);
+  // fused append: the token-storing workgroups after the decode's (FP8:
+  // merge_kernel stores them)
+  const int64_t nappend =
+      P.fused && d.kv_dtype != PKV_FP8_E4M3 ? (a->batch + P.append_spg - 1) / P.append_spg : 0;
   if (P.shared > 0) {
-    decode_fn pfn = pick_prefix(d.kv_dtype, d.head_dim, d.block_size);
+    prefix_fn pfn = pick_prefix(d.kv_dtype, d.head_dim, d.block_size);
     if (!pfn) return fail(PKV_E_UNSUPPORTED, "no kernel for this shape");
     const int64_t tasks = (int64_t)d.num_kv_heads * P.pre_rtiles * P.pre_chunks;
     const int64_t pgrid = ((tasks + 7) / 8) * 8;  // one workgroup per task, whole rounds over the 8 XCDs
@@ -2412,21 +2589,23 @@ static pkv_status decode_launch(const kv_pool* pool, const paged_decode_args* a,
     ev_first = nullptr;
   }
 
-  const decode_fn mfn = d.head_dim == 64 ? pick_merge<64>(P) : pick_merge<128>(P);
+  const tail_fn mfn = d.head_dim == 64 ? pick_merge<64>(P) : pick_merge<128>(P);
   if (single) {
     P.single = 1;
     P.num_waves = 0;
     if (P.allpart) P.ws_job = reinterpret_cast<int4*>(ws + wl.job_off);
     const int64_t grid = (segs + 3) / 4;
-    e = launch(fn, dim3((uint32_t)grid), 0, s, ev_first, ev ? ev[1] : nullptr, P);
+    TP.decode_wgs = (int32_t)grid;
+    e = afn ? launch(afn, dim3((uint32_t)(grid + nappend)), 0, s, ev_first, ev ? ev[1] : nullptr, P, TP)
+            : launch(fn, dim3((uint32_t)grid), 0, s, ev_first, ev ? ev[1] : nullptr, P);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     if (nk) *nk = 1;
     if (!P.fused) return PKV_OK;
     // the fused append's merge: every pair's own partial and the new token,
-    // and the workgroups that store the new tokens
+    // and the workgroups that write the rows' tables and lengths
     P.merge_pg = 1;
-    const int64_t mgrid = segs + (a->batch + P.append_spg - 1) / P.append_spg;
-    e = launch(mfn, dim3((uint32_t)mgrid), 0, s, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, P);
+    const int64_t mgrid = segs + merge_row_groups(P);
+    e = launch(mfn, dim3((uint32_t)mgrid), 0, s, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, P, TP);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
     if (nk) *nk = 2;
     return PKV_OK;
@@ -2448,7 +2627,9 @@ static pkv_status decode_launch(const kv_pool* pool, const paged_decode_args* a,
   const int64_t per_slot = 4 * (int64_t)(4 * P.group * (d.head_dim + 8) + (int64_t)sizeof(PieceTag));
   P.nstage = (int32_t)std::max<int64_t>(0, std::min<int64_t>(4, (63488 - P.stage_off) / per_slot));
   const size_t lds = (size_t)P.stage_off + (size_t)P.nstage * per_slot;
-  e = launch(fn, dim3((uint32_t)grid), lds, s, ev_first, ev ? ev[1] : nullptr, P);
+  TP.decode_wgs = (int32_t)grid;
+  e = afn ? launch(afn, dim3((uint32_t)(grid + nappend)), lds, s, ev_first, ev ? ev[1] : nullptr, P, TP)
+          : launch(fn, dim3((uint32_t)grid), lds, s, ev_first, ev ? ev[1] : nullptr, P);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   if (nk) *nk = 1;
   // few sequence-heads: spread each one's output positions over several
@@ -2457,8 +2638,8 @@ static pkv_status decode_launch(const kv_pool* pool, const paged_decode_args* a,
   int pg = 1;
   while (segs * pg < 512 && np / (pg * 2) >= 16) pg *= 2;
   P.merge_pg = pg;
-  const int64_t mgrid = segs * pg + (P.fused ? (a->batch + P.append_spg - 1) / P.append_spg : 0);
-  e = launch(mfn, dim3((uint32_t)mgrid), 0, s, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, P);
+  const int64_t mgrid = segs * pg + (P.fused ? merge_row_groups(P) : 0);
+  e = launch(mfn, dim3((uint32_t)mgrid), 0, s, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, P, TP);
   if (e != hipSuccess) return hip_fail(e, "merge launch");
   if (nk) *nk = 2;
   return PKV_OK;
