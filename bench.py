@@ -4,11 +4,12 @@ One step is one pass of the whole decode hot path over one batch:
   1. host: reserve one slot per sequence (block_table_append_batch: on-demand
      blocks, copy-on-write of shared partial blocks),
   2. paged_attention_decode with the fused append: the range-split decode of
-     the cached tokens, then the log-sum-exp merge, which folds in the new
-     token and writes it into its slot, the row's table entry and length
-     (device-resident tables; the slots are read from the page-locked buffer
-     the host wrote them to).  Forked families, whose tables change every
-     step, first export and upload the step's metadata and copy the
+     the cached tokens, whose last workgroups store the new tokens into their
+     slots (FP8 pools: the merge stores them), then the log-sum-exp merge,
+     which folds in the new token and writes the row's table entry and
+     length (device-resident tables; the slots are read from the page-locked
+     buffer the host wrote them to).  Forked families, whose tables change
+     every step, first export and upload the step's metadata and copy the
      copy-on-write blocks.  --unfused runs paged_kv_append_step (or
      paged_kv_append) before a plain decode instead.
 Inputs (the cache and every step's q, k, v) are resident in HBM before the
@@ -16,12 +17,13 @@ timed region starts.  Several independently placed copies of the cache are
 rotated so the working set is several times the 256 MB Infinity Cache.
 
 Prints one JSON line.  ``value`` is KV GB/s over the whole step (algorithmic
-bytes of the decode / step time).  ``roofline`` is the dominant kernel,
-decode_kernel, alone: its algorithmic bytes (everything the call must move
-except the output, which the merge writes) over its own launch duration,
-recorded by the kernel's start and end events on the launch stream;
-``roofline.call_*`` and ``decode_ms`` / ``decode_GBps`` are the whole call
-(decode_kernel + merge_kernel).  With a shared prefix the three kernels of
+bytes of the decode / step time).  ``roofline`` is the dominant kernel
+(decode_append_kernel, or decode_kernel for FP8 and unfused runs) alone: its
+algorithmic bytes (everything the decode must move except the output, which
+the merge writes, plus the new tokens it stores) over its own launch
+duration, recorded by the kernel's start and end events on the launch
+stream; ``roofline.call_*`` and ``decode_ms`` / ``decode_GBps`` are the whole
+call (decode + merge, with the append's bytes).  With a shared prefix the three kernels of
 the call are one unit and ``roofline`` is the call.  With the default
 workload (c3), ``targets`` holds the same figures for the 128K-context
 workloads (bf16 and FP8 KV), measured by shorter runs in the same process.
@@ -190,6 +192,19 @@ def decode_bytes(w, lengths):
     return total, kv
 
 
+def new_token_bytes(w, batch):
+    """The new tokens of a fused call: each row's K and V read in the source
+    dtype and written into the pool."""
+    return batch * w.num_kv_heads * w.head_dim * 2 * (wl.ELEM_BYTES[w.src_dtype] + wl.ELEM_BYTES[w.kv_dtype])
+
+
+def append_bytes(w, batch):
+    """Algorithmic bytes of a fused call's append: the new tokens, each row's
+    slot read (8 B), its length read and written and its table entry written
+    (12 B)."""
+    return new_token_bytes(w, batch) + batch * (8 + 12)
+
+
 class Replica:
     """One independently placed copy of the workload's cache."""
 
@@ -332,6 +347,7 @@ def run(args):
     ring = []
     for _ in range(RING):
         buf = torch.empty(reps[0].n_meta, dtype=torch.int32, pin_memory=True)
+        buf.numpy().fill(0)     # touched once here, not first inside a timed step
         ring.append((buf, buf.numpy()))
     mb = reps[0].max_blocks
     meta_bytes = reps[0].n_meta * 4
@@ -365,10 +381,16 @@ def run(args):
     # fence (see HipEvent); an event still costs a little, so only a sample
     # of steps carries them.  The last event of a sampled step also tells the
     # host that the kernels up to that step have finished reading the
-    # page-locked staging buffers (staging ring reuse).
+    # page-locked staging buffers (staging ring reuse).  The first timed step
+    # is not sampled (unless it is the only one): a call with events costs
+    # the host tens of microseconds more, the first one over a hundred, and
+    # at the start of the timed region the device would wait for them.
     TIME_EVERY = 8
-    sampled = {t: [HipEvent() for _ in range(4)]
-               for t in sorted(set(range(0, n_total, TIME_EVERY)) | {args.warmup})}
+    PHASE = (args.warmup + 1) % TIME_EVERY
+    sample_steps = set(range(PHASE, n_total, TIME_EVERY))
+    if not any(t >= args.warmup for t in sample_steps):
+        sample_steps.add(args.warmup)
+    sampled = {t: [HipEvent() for _ in range(4)] for t in sorted(sample_steps)}
     torch.cuda.synchronize()
     n_kernels = {}
     step_lens = {}
@@ -392,7 +414,7 @@ def run(args):
             # the oldest sampled step at or after t - RING: its end implies that
             # step t - RING's upload (the last reader of this buffer) has run,
             # and the host may stay several steps ahead of the device
-            f = TIME_EVERY * ((t - RING + TIME_EVERY - 1) // TIME_EVERY)
+            f = (t - RING) + (PHASE - (t - RING)) % TIME_EVERY
             sampled[f][3 if n_kernels[f] == 2 else 1].synchronize()
         slots_np = npb[: 2 * B].view(np.int64)
         cows_np = npb[2 * B: 4 * B].reshape(B, 2)
@@ -441,15 +463,16 @@ def run(args):
             # of any later reuse of the freed blocks
             P.block_table_free_batch(h, seqs)
 
+    # no garbage-collector pass inside the timed loop: a full pass over this
+    # process's objects takes tens of milliseconds.  Collected before the
+    # warm-up, whose steps then bring the host's caches back.
+    gc.collect()
+    gc.freeze()
+    gc.disable()
     log(f"warmup {args.warmup} steps")
     for t in range(args.warmup):
         step(t, False)
     torch.cuda.synchronize()
-    # no garbage-collector pass inside the timed loop: a full pass over this
-    # process's objects takes tens of milliseconds
-    gc.collect()
-    gc.freeze()
-    gc.disable()
     log(f"timing {args.steps} steps")
     t_start = torch.cuda.Event(enable_timing=True)
     t_stop = torch.cuda.Event(enable_timing=True)
@@ -522,15 +545,24 @@ def run(args):
     elif traffic is not None:
         traffic_source = (f"stored calibration, not read in this run: rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE "
                           f"of this kernel source (kernels_sha {kernels_sha()}) scaled by a plain 1 GiB copy")
-    achieved = s_bytes / (avg_dec_ms * 1e-3) / 1e9
+    # the call's bytes: the decode's, and with a fused append the new tokens'
+    call_bytes = s_bytes + (append_bytes(w, B) if fused else 0)
+    achieved = call_bytes / (avg_dec_ms * 1e-3) / 1e9
     avg_kern_ms = float(np.mean(kern_ms))
+    # with a fused append into a pool other than FP8 the first kernel is
+    # decode_append_kernel, which also stores the new tokens (K and V read and
+    # written, the slot read and copied for the merge)
+    tail_append = fused and w.kv_dtype != "fp8"
+    decode_name = "decode_append_kernel" if tail_append else "decode_kernel"
     if prefix:
         # prefix, suffix and merge kernels work as one: the roofline is the call
-        r_kernel, r_ms, r_bytes = ("paged_attention_decode (prefix_kernel + decode_kernel + merge_kernel)",
-                                   avg_dec_ms, s_bytes)
+        r_kernel, r_ms, r_bytes = (f"paged_attention_decode (prefix_kernel + {decode_name} + merge_kernel)",
+                                   avg_dec_ms, call_bytes)
     else:
         s_out = float(np.mean([out_bytes(w, step_lens[t]) for t in timed]))
-        r_kernel, r_ms, r_bytes = "decode_kernel", avg_kern_ms, s_bytes - s_out
+        # decode_append_kernel: the new tokens, each slot read and copied
+        tail = new_token_bytes(w, B) + 16 * B if tail_append else 0
+        r_kernel, r_ms, r_bytes = decode_name, avg_kern_ms, s_bytes - s_out + tail
     r_achieved = r_bytes / (r_ms * 1e-3) / 1e9
     res = {
         "metric": METRIC,
@@ -780,7 +812,8 @@ def main():
                 "call_frac": r["roofline"]["call_frac"], "seq_heads_per_s": r["decode_seq_heads_per_s"],
                 "traffic": r["roofline"]["traffic"], "traffic_source": r["roofline"]["traffic_source"],
             }
-            log(f"{name}: decode_kernel {r['roofline']['launch_ms']:.4f} ms, frac {r['roofline']['frac']:.3f}; "
+            res["targets"][name]["kernel"] = r["roofline"]["kernel"]
+            log(f"{name}: {r['roofline']['kernel']} {r['roofline']['launch_ms']:.4f} ms, frac {r['roofline']['frac']:.3f}; "
                 f"call {r['roofline']['call_ms']:.4f} ms, frac {r['roofline']['call_frac']:.3f}")
     # context for the roofline: what a plain streaming read of 2 GiB reaches
     # on this device (pkv_hbm_read_probe, median of 10 calls)
