@@ -63,19 +63,20 @@ WORKLOAD_NAMES = {
 }
 
 
-# HBM bytes per decode_kernel launch (read + write), from rocprofv3 --pmc
+# HBM bytes per launch of the dominant kernel (decode_append_kernel, or
+# decode_kernel for FP8; read + write), from rocprofv3 --pmc
 # FETCH_SIZE and WRITE_SIZE runs scaled by what the same counters read for a
 # plain 1 GiB device copy (FETCH x 2.0, WRITE x 1.0).  Each entry holds for the
 # kernel source it was measured on (kernels_sha()); for any other source the
 # figure is not reported.
 MEASURED_TRAFFIC = {
-    "c3": (507.0e6, "6c4469231ea0c88c"),
-    "c2": (1981.3e6, "6c4469231ea0c88c"),
-    "c2_bs128": (2039.3e6, "6c4469231ea0c88c"),
-    "c5": (2158.5e6, "6c4469231ea0c88c"),
-    "c5_fp8": (1080.5e6, "6c4469231ea0c88c"),
-    "c5w": (72.3e6, "6c4469231ea0c88c"),
-    "c4": (383.6e6, "6c4469231ea0c88c"),   # the whole call: prefix, suffix and merge kernels
+    "c3": (511.5e6, "e53bd533a46f983b"),
+    "c2": (1990.2e6, "e53bd533a46f983b"),
+    "c2_bs128": (2047.8e6, "e53bd533a46f983b"),
+    "c5": (2158.5e6, "e53bd533a46f983b"),
+    "c5_fp8": (1080.5e6, "e53bd533a46f983b"),
+    "c5w": (72.1e6, "e53bd533a46f983b"),
+    "c4": (390.7e6, "e53bd533a46f983b"),   # the whole call: prefix, suffix and merge kernels
 }
 
 
