@@ -79,8 +79,9 @@ class FusedState:
         self.d_lens = torch.from_numpy(ln).cuda()
         torch.cuda.synchronize()
 
-    def step(self, t, splits, window=0, pinned=True, drop_row=None):
-        """One fused step; returns (gpu output, oracle output)."""
+    def step(self, t, splits, window=0, pinned=True, drop_row=None, static=False):
+        """One fused step; returns (gpu output, oracle output).  static: through
+        paged_attention_decode_static (the library's own workspace)."""
         w, h = self.w, self.pool.handle
         B = len(self.seqs)
         slots, cows = P.block_table_append_batch(h, self.seqs)
@@ -98,11 +99,14 @@ class FusedState:
         a = P.make_decode_args(0, B, w.num_q_heads, self.mb, to_dev(qb), w.q_dtype, self.d_tables, self.d_lens,
                                1.0 / math.sqrt(w.head_dim), out, "f32", sliding_window=window, num_splits=splits,
                                new_k=kd, new_v=vd, new_dtype=w.src_dtype, new_slots=d_slots)
-        nbytes = P.paged_attention_workspace_size(h, a)
-        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
-        a.workspace, a.workspace_bytes = ws.data_ptr(), nbytes
-        a._refs = a._refs + (ws,)
-        P.paged_attention_decode(h, a)
+        if static:
+            P.paged_attention_decode_static(h, a)
+        else:
+            nbytes = P.paged_attention_workspace_size(h, a)
+            ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+            a.workspace, a.workspace_bytes = ws.data_ptr(), nbytes
+            a._refs = a._refs + (ws,)
+            P.paged_attention_decode(h, a)
         torch.cuda.synchronize()
         got = out_to_f64(out, "f32")
         # oracle: the same token appended, then plain attention over L + 1

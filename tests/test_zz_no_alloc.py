@@ -5,8 +5,9 @@ Both run the same kernels on the same arguments, so their outputs must be
 identical bit for bit; both are also held to the oracle at the usual bar
 (2e-3 max-abs, bf16 KV).  Two calls in a row, the second with a smaller
 input, then a shared-prefix call (the workspace then also holds the prefix
-partials); a call needing more than the static workspace, and a call that
-brings its own workspace, are refused on the host before any launch.
+partials) and fused-append steps (bf16 and FP8 pools); a call needing more
+than the static workspace, and a call that brings its own workspace, are
+refused on the host before any launch.
 """
 import math
 
@@ -93,6 +94,28 @@ def test_static_workspace_shared_prefix_decode_matches():
         st.check(static, st.reference(q, otables, olens))
     finally:
         st.close()
+
+
+@pytest.mark.parametrize("name", ["gqa8_bf16", "gqa8_fp8"])
+def test_static_workspace_fused_append_matches(name):
+    # the fused append through both entry points, on two identical states:
+    # outputs, device tables and lengths, and both pools bit for bit, over
+    # two consecutive steps
+    from test_gpu_fused_append import CASES, FusedState, TOL
+    w = CASES[name]
+    d = wl.draw(w, extra_blocks=w.batch * 2)
+    a, b = FusedState(w, d), FusedState(w, d)
+    try:
+        for t in range(2):
+            got_ws, ref = a.step(t, 0)
+            got_static, _ = b.step(t, 0, static=True)
+            assert np.array_equal(got_static, got_ws), (name, t)
+            assert np.abs(got_static - ref).max() <= TOL[w.kv_dtype]
+            assert torch.equal(a.d_tables, b.d_tables) and torch.equal(a.d_lens, b.d_lens)
+            assert torch.equal(a.pool.k_cache, b.pool.k_cache) and torch.equal(a.pool.v_cache, b.pool.v_cache)
+    finally:
+        a.close()
+        b.close()
 
 
 def test_static_workspace_refusals_on_the_host():
