@@ -485,6 +485,48 @@ __device__ void scan_units(const DecodeParams& P, int32_t* C) {
   __syncthreads();
 }
 
+// scan_units with the 256-wide scan done by lane exchanges inside each
+// wavefront and one pass over the four wavefront totals: two barriers
+// instead of sixteen.  Used by decode_append_kernel (decode_kernel keeps
+// scan_units, see decode_body).
+template <int BS, int U>
+__device__ void scan_units_wave(const DecodeParams& P, int32_t* C) {
+  __shared__ int32_t wsum[4];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int per = (P.batch + 255) / 256;
+  const int b0 = tid * per;
+  const int b1 = min(P.batch, b0 + per);
+  int32_t local = 0;
+  for (int b = b0; b < b1; ++b) {
+    const int32_t raw = P.lens[b];
+    int32_t L, lo, first, nu;
+    extent_of<BS, U>(P, raw, &L, &lo, &first, &nu);
+    C[b] = nu;
+    if (P.lens_in_lds) C[P.batch + 1 + b] = raw;
+    local += nu;
+  }
+  int32_t x = local;   // inclusive scan over the wavefront's lanes
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wsum[wv] = x;
+  __syncthreads();
+  int32_t before = 0;
+  for (int k = 0; k < wv; ++k) before += wsum[k];
+  const int32_t incl = before + x;
+  int32_t run = incl - local;
+  for (int b = b0; b < b1; ++b) {
+    const int32_t nu = C[b];
+    C[b] = run;
+    run += nu;
+  }
+  if (tid == 255) C[P.batch] = incl;
+  __syncthreads();
+}
+
 __device__ __forceinline__ int64_t range_start(int64_t w, int64_t T, int64_t W) { return w * T / W; }
 
 // The wavefront whose range holds unit x (every range is non-empty: W <= T).
@@ -1596,7 +1638,7 @@ __device__ __forceinline__ void decode_body(DecodeParams P, uint32_t nwg) {
     return;
   }
 
-  scan_units<BS, U>(P, C);
+  scan_units_wave<BS, U>(P, C);
   const int64_t t_head = C[P.batch];
   const int64_t T = t_head * P.hkv;
   // sequences with nothing to attend get zero rows
