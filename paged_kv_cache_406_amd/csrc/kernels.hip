@@ -603,6 +603,38 @@ __device__ __forceinline__ void wait_stages(int a) {
   }
 }
 
+// Entries rel .. rel + UB - 1 of a block-table row of n >= 1 entries (-1 from
+// n on), read with scalar loads; rel is wave-uniform.  Scalar loads are
+// counted by lgkmcnt, so waiting for them leaves the vector loads in flight
+// alone (a vector load of a table entry inside a loop of untracked
+// global-to-LDS loads makes the compiler wait for every load).  Each index
+// is clamped into the row before it is read.
+template <int UB>
+__device__ __forceinline__ void table_entries_scalar(const int32_t* row, int32_t rel, int32_t n,
+                                                     int32_t (&ids)[UB]) {
+  static_assert(UB == 1 || UB == 2 || UB == 4, "blocks per unit");
+  uint32_t off[UB];
+#pragma unroll
+  for (int k = 0; k < UB; ++k) off[k] = 4u * (uint32_t)(rel + k < n ? rel + k : n - 1);
+  if constexpr (UB == 1) {
+    asm volatile("s_load_dword %0, %1, %2\n\ts_waitcnt lgkmcnt(0)" : "=&s"(ids[0]) : "s"(row), "s"(off[0]) : "memory");
+  } else if constexpr (UB == 2) {
+    asm volatile("s_load_dword %0, %2, %3\n\ts_load_dword %1, %2, %4\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&s"(ids[0]), "=&s"(ids[1])
+                 : "s"(row), "s"(off[0]), "s"(off[1])
+                 : "memory");
+  } else {
+    asm volatile(
+        "s_load_dword %0, %4, %5\n\ts_load_dword %1, %4, %6\n\ts_load_dword %2, %4, %7\n\t"
+        "s_load_dword %3, %4, %8\n\ts_waitcnt lgkmcnt(0)"
+        : "=&s"(ids[0]), "=&s"(ids[1]), "=&s"(ids[2]), "=&s"(ids[3])
+        : "s"(row), "s"(off[0]), "s"(off[1]), "s"(off[2]), "s"(off[3])
+        : "memory");
+  }
+#pragma unroll
+  for (int k = 0; k < UB; ++k) ids[k] = rel + k < n ? ids[k] : -1;
+}
+
 // LDS slots of the shared-prefix pipeline (16 KiB each); two workgroups of
 // prefix_kernel share a CU
 #ifndef PKV_PREFIX_STAGES
@@ -885,22 +917,33 @@ struct Decoder {
     if (!tile_full(T, lo, L, kg)) {
       int32_t base = T.tok0 + TPG * kg;   // kept below the branch (see softmax)
       asm volatile("" : "+v"(base));
-      uint32_t vmask[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int e = 0; e < TPG; ++e) {
-        const int32_t tok = base + e;
-        const bool valid = T.ok && tok >= lo && tok < L;
-        const uint32_t field = EB == 4 ? 0xffffffffu : (EB == 2 ? 0xffffu : 0xffu);
-        vmask[e / EPW] |= valid ? field << (8 * EB * (e % EPW)) : 0u;
-      }
-#pragma unroll
-      for (int n = 0; n < NV; ++n) {
-        T.v[n].x &= vmask[0];
-        T.v[n].y &= vmask[1];
-        T.v[n].z &= vmask[2];
-        T.v[n].w &= vmask[3];
-      }
+      mask_v(T, base, lo, L);
     }
+    pv_acc(T, p, st);
+  }
+
+  // Zero the V elements of this lane's tokens base .. base + TPG - 1 that
+  // are not attended (outside [lo, L), or not in a real block).
+  static __device__ __forceinline__ void mask_v(VTile& T, int32_t base, int32_t lo, int32_t L) {
+    uint32_t vmask[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < TPG; ++e) {
+      const int32_t tok = base + e;
+      const bool valid = T.ok && tok >= lo && tok < L;
+      const uint32_t field = EB == 4 ? 0xffffffffu : (EB == 2 ? 0xffffu : 0xffu);
+      vmask[e / EPW] |= valid ? field << (8 * EB * (e % EPW)) : 0u;
+    }
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+      T.v[n].x &= vmask[0];
+      T.v[n].y &= vmask[1];
+      T.v[n].z &= vmask[2];
+      T.v[n].w &= vmask[3];
+    }
+  }
+
+  // The MFMA part of pv: O += P.V with V already masked.
+  static __device__ __forceinline__ void pv_acc(const VTile& T, const float (&p)[NQT][4], State& st) {
     if constexpr (KV == KV_F32) {
 #pragma unroll
       for (int n = 0; n < NV; ++n) {
@@ -1154,6 +1197,79 @@ struct Decoder {
   static constexpr int STAGE_BYTES = (KG + VG) * 16;
   static constexpr int STAGES = PKV_PREFIX_STAGES;
 
+  // Maximum of v over the four lanes of a query row (lanes i, i + 16, i + 32,
+  // i + 48): each swap leaves a lane's own value in one result and its
+  // partner's (lane ^ 32, then lane ^ 16) in the other.
+  static __device__ __forceinline__ float row_max4(float v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  }
+
+  // Online softmax of one row tile of the shared prefix (the decode's
+  // softmax with the masking decided per sub-tile by the caller): with MASK,
+  // tokens at or past the row's L, or in a block that is not real, get
+  // probability 0.
+  template <bool MASK>
+  static __device__ __forceinline__ void prefix_softmax(const VTile& T, const f32x4 (&S)[NQT], State& st,
+                                                        float (&p)[NQT][4], int32_t L, float scale_log2, int kg) {
+    float s[NQT][4];
+#pragma unroll
+    for (int t = 0; t < NQT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        s[t][r] = S[t][r] * scale_log2;
+        if constexpr (MASK) {
+          const int32_t tok = T.tok0 + TPG * kg + 4 * t + r;
+          s[t][r] = T.ok && tok < L ? s[t][r] : -INFINITY;
+        }
+      }
+    float bmax = s[0][0];
+#pragma unroll
+    for (int t = 0; t < NQT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) bmax = fmaxf(bmax, s[t][r]);
+    bmax = row_max4(bmax);
+    const bool up = bmax > st.m + RESCALE_LOG2;   // the first finite score always moves it
+    if (__any(up)) {
+      const float alpha = up ? __builtin_amdgcn_exp2f(st.m - bmax) : 1.0f;
+      st.m = up ? bmax : st.m;
+      st.l *= alpha;
+#pragma unroll
+      for (int n = 0; n < NV; ++n) st.O[n] *= alpha;
+    }
+    const float m_use = st.m == -INFINITY ? 0.f : st.m;
+    float psum = 0.f;
+#pragma unroll
+    for (int t = 0; t < NQT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[t][r] = __builtin_amdgcn_exp2f(s[t][r] - m_use);
+        psum += p[t][r];
+      }
+    st.l += psum;
+  }
+
+  // One staged sub-tile of the shared prefix for this wavefront's NT row
+  // tiles: scores and softmax of each tile, then P.V of each.  Without MASK
+  // every token is attended by every row.
+  template <bool MASK>
+  static __device__ __forceinline__ void prefix_step(const KTile& K, VTile& V, const qop (&q)[NT][NQ],
+                                                     State (&st)[NT], const int32_t (&Lc)[NT], int32_t kT,
+                                                     float scale_log2, int kg) {
+    f32x4 S[NQT];
+    float pp[NT][NQT][4];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      qk(K, q[t], S);
+      prefix_softmax<MASK>(V, S, st[t], pp[t], Lc[t], scale_log2, kg);
+    }
+    if constexpr (MASK) mask_v(V, V.tok0 + TPG * kg, 0, kT);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) pv_acc(V, pp[t], st[t]);
+  }
+
   // Shared prefix, one workgroup of 4 wavefronts: query rows
   // rg*64*NT .. +64*NT of KV head g (wavefront wv takes 16*NT of them; row
   // r = sequence r / G, head g*G + r % G) against token chunk c of the prefix
@@ -1197,26 +1313,18 @@ struct Decoder {
     const int32_t s0 = (int32_t)((int64_t)c * nsp / P.pre_chunks);
     const int32_t s1 = (int32_t)((int64_t)(c + 1) * nsp / P.pre_chunks);
 
-    // row 0's table entries of the prefix, 64 at a time, one per lane; one
-    // cache for the loads and one for the math, which run two sub-tiles apart
-    struct TabCache {
-      int cc = -1;
-      int32_t t = -1;
-    } tab_load, tab_math;
-    // the addresses this lane would load sub-tile s from
-    auto where = [&](int32_t s, TabCache& tc) -> Addr {
+    // the addresses this lane would load sub-tile s from (row 0's table
+    // entries of the prefix, read with scalar loads)
+    auto where = [&](int32_t s) -> Addr {
       const int32_t tok = s * TT;
       const int32_t rel = (tok / U) * UB;  // first table entry of the unit
-      const int cc = rel >> 6;
-      if (cc != tc.cc) {
-        tc.t = table_chunk(P, 0, 0, P.shared, cc, lane);
-        tc.cc = cc;
-      }
       int32_t ids[UB];
-#pragma unroll
-      for (int k = 0; k < UB; ++k) ids[k] = __builtin_amdgcn_readlane(tc.t, (rel & 63) + k);
+      table_entries_scalar<UB>(P.tables, rel, P.shared, ids);
       return locate(P, g, ids, (tok % U) / TT, tok, i, kg);
     };
+    // bit x: this lane's V block of the sub-tile staged in slot x is a real
+    // block (recorded when its loads are issued, read by the math)
+    uint32_t okbits = 0;
     // Stage sub-tile s in LDS slot `slot` with global-to-LDS loads: the
     // workgroup's 256 threads move its KG + VG 16-byte groups, group
     // x = 256u + 64 * wave + lane being load x / 64 of lane x % 64 (K loads
@@ -1226,7 +1334,8 @@ struct Decoder {
     constexpr int NG = (KG + VG) / 256;
     const uint32_t lds0 = uniform((uint32_t)(uintptr_t)lds);
     auto issue = [&](int32_t s, int slot) {
-      const Addr a = where(s, tab_load);
+      const Addr a = where(s);
+      okbits = a.ok ? okbits | (1u << slot) : okbits & ~(1u << slot);
 #pragma unroll
       for (int u = 0; u < NG; ++u) {
         const int x0 = 256 * u + 64 * wv;  // uniform
@@ -1241,41 +1350,66 @@ struct Decoder {
       }
     };
 
+    // Sub-tiles below s_full need no masking in this wavefront: every live
+    // row attends all of their tokens (rows that are not live produce
+    // nothing, whatever they compute), and all their blocks are real.
+    int32_t lmin = INT32_MAX;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) lmin = min(lmin, live[t] ? Lc[t] : INT32_MAX);
+#pragma unroll
+    for (int x = 1; x < 64; x <<= 1) lmin = min(lmin, __shfl_xor(lmin, x));
+    int32_t s_full = uniform(lmin / TT);
+    {
+      // the first table entry of the chunk that is not a real block
+      const int32_t e0 = (int32_t)((int64_t)s0 * TT / BS);
+      const int32_t e1 = min(P.shared, (int32_t)(((int64_t)s1 * TT + BS - 1) / BS));
+      for (int32_t e = e0; e < e1; e += 64) {
+        const int32_t k = e + lane;
+        const int32_t id = k < e1 ? P.tables[k] : 0;
+        const uint64_t bad = __ballot(k < e1 && (id < 0 || id >= P.num_blocks));
+        if (bad) {
+          s_full = min(s_full, (int32_t)((int64_t)(e + __builtin_ctzll(bad)) * BS / TT));
+          break;
+        }
+      }
+    }
+
     if (s0 < s1) {
       // STAGES LDS slots: STAGES - 1 sub-tiles in flight while one is used;
       // sub-tile x lives in slot (x - s0) % STAGES
       for (int k = 0; k < STAGES - 1 && s0 + k < s1; ++k) issue(s0 + k, k);
-      KTile K;
-      VTile V;
-      f32x4 S[NQT];
-      float pp[NT][NQT][4];
       int slot = 0;
-      for (int32_t s = s0; s < s1; ++s) {
-        // the slot of sub-tile s - 1 was last read in iteration s - 1,
-        // before its closing barrier
-        if (s + STAGES - 1 < s1) issue(s + STAGES - 1, slot == 0 ? STAGES - 1 : slot - 1);
-        // sub-tile s has landed once no more than `ahead` stages (NG loads
-        // each) are outstanding: this thread's, then every thread's
-        const int ahead = min(STAGES - 1, s1 - 1 - s);
-        wait_stages<NG, STAGES - 1>(ahead);
+      // Sub-tile s into K and V.  It has landed once no more than `ahead`
+      // stages (NG loads each) are outstanding: this thread's, then (barrier)
+      // every thread's.  After the barrier every wavefront is also done with
+      // the slot of sub-tile s - 1, which the next issue refills.
+      auto next = [&](int32_t s, KTile& K, VTile& V) {
+        const int ahead = min(STAGES - 2, s1 - 1 - s);
+        wait_stages<NG, STAGES - 2>(ahead);
         __syncthreads();
+        if (s + STAGES - 1 < s1) issue(s + STAGES - 1, slot == 0 ? STAGES - 1 : slot - 1);
         const uint4* src = reinterpret_cast<const uint4*>(lds + slot * STAGE_BYTES);
 #pragma unroll
         for (int m = 0; m < NKL; ++m) K.k[m] = src[m * 64 + lane];
 #pragma unroll
         for (int n = 0; n < NV; ++n) V.v[n] = src[KG + n * 64 + lane];
-        const Addr a = where(s, tab_math);
-        V.tok0 = a.tok0;
-        V.ok = a.ok;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          qk(K, q[t], S);
-          softmax(V, S, st[t], pp[t], 0, Lc[t], P.scale_log2, kg);
-        }
-#pragma unroll
-        for (int t = 0; t < NT; ++t) pv(V, pp[t], st[t], 0, kT, kg);
-        __syncthreads();   // every wavefront is done with this slot
+        V.tok0 = s * TT;
+        V.ok = ((okbits >> slot) & 1u) != 0;
         slot = slot == STAGES - 1 ? 0 : slot + 1;
+      };
+      // the sub-tiles that need no masking, then the rest
+      const int32_t s_mid = max(s0, min(s1, s_full));
+      for (int32_t s = s0; s < s_mid; ++s) {
+        KTile K;
+        VTile V;
+        next(s, K, V);
+        prefix_step<false>(K, V, q, st, Lc, kT, P.scale_log2, kg);
+      }
+      for (int32_t s = s_mid; s < s1; ++s) {
+        KTile K;
+        VTile V;
+        next(s, K, V);
+        prefix_step<true>(K, V, q, st, Lc, kT, P.scale_log2, kg);
       }
     }
 
