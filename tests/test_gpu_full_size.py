@@ -124,12 +124,17 @@ class FullState:
             list(ex.map(lambda t: self.opool.append(0, t[0], t[1], src, t[2]), self._pending))
         self._pending = []
 
-    def decode(self, seqs, oseqs, q, shared=0, splits=0):
+    def decode(self, seqs, oseqs, q, shared=0, splits=0, edit=None):
+        """edit(tables, lens) -> (tables, lens), if given, changes the exported
+        tables and lengths (both sides' copies) before the call."""
         w = self.w
         mb = max(len(self.bm.table(o)) for o in oseqs)
         tables, lens = P.block_table_export(self.pool.handle, seqs, mb)
         otables, olens = self.bm.export(oseqs, mb)
         assert np.array_equal(tables, otables) and np.array_equal(lens, olens)
+        if edit is not None:
+            tables, lens = edit(tables.copy(), lens.copy())
+            otables, olens = tables.copy(), lens.copy()
         B = len(seqs)
         out = torch.full((B, w.num_q_heads, w.head_dim), float("nan"), dtype=torch.float32, device="cuda")
         qd, td, ld = to_dev(q), torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda()

@@ -8,6 +8,8 @@ the oracle), and the decode that reads those blocks once for the whole batch
 is compared with the oracle's plain attention on every row, for several split
 counts, and with the ordinary decode of the same state.
 """
+import math
+
 import numpy as np
 import pytest
 
@@ -61,6 +63,76 @@ def test_shared_prefix_decode_parity(name):
         if k > 1:
             got, _, _ = st.decode(st.seqs, st.oseqs, q, shared=k // 2)
             st.check(got, ref)
+    finally:
+        st.close()
+
+
+def _reference_skipping(st, q, tables, lens):
+    """The decode's result when table entries outside the pool are empty
+    blocks whose tokens are skipped (the decode's documented reading of such
+    entries): per row, KV head and query head, the oracle's partial over the
+    attended tokens of each real block, joined by the oracle's log-sum-exp
+    merge."""
+    from oracle.attention import lse_merge, partial_attention
+    from oracle.pool import bits_to_f64
+    w, pool, bs = st.w, st.opool, st.w.block_size
+    qf = bits_to_f64(q, w.q_dtype)
+    B, Hq, D = qf.shape
+    G = Hq // w.num_kv_heads
+    scale = 1.0 / math.sqrt(w.head_dim)
+    out = np.zeros((B, Hq, D))
+    for b in range(B):
+        L = int(lens[b])
+        for g in range(w.num_kv_heads):
+            parts = {h: [] for h in range(g * G, (g + 1) * G)}
+            for j in range(-(-L // bs)):
+                blk = int(tables[b, j])
+                if blk < 0 or blk >= pool.num_blocks:
+                    continue
+                n = min(bs, L - j * bs)
+                K = pool.values("k", 0, [blk], g)[:n]
+                V = pool.values("v", 0, [blk], g)[:n]
+                for h in parts:
+                    parts[h].append(partial_attention(qf[b, h], K, V, scale))
+            for h, pr in parts.items():
+                if pr:
+                    out[b, h] = lse_merge(pr)
+    return out
+
+
+@pytest.mark.parametrize("name", ["bf16_g4", "fp8_g8", "bf16_bs128_d64"])
+def test_shared_prefix_short_rows_and_empty_blocks(name):
+    # Rows that end inside the shared run (at a sub-tile edge, inside a
+    # sub-tile, near its start, at 0), and entries of the shared run that are
+    # not real blocks (the same in every row, as the contract asks), which
+    # make the prefix pass mask sub-tiles before the end of its chunk.
+    w, d, st = _family(name)
+    try:
+        k = P.block_table_common_prefix(st.pool.handle, st.seqs)
+        kT = k * w.block_size
+        q = wl.q_bits(w)
+
+        def short(tables, lens):
+            for r, L in zip(range(1, len(lens), 2), (kT - 5, 32, 3, 0, kT - 1)):
+                lens[r] = max(0, min(L, kT))
+            return tables, lens
+
+        for splits in (0, 7):
+            got, ot, ol = st.decode(st.seqs, st.oseqs, q, shared=k, splits=splits, edit=short)
+            assert (ol < kT).any()
+            st.check(got, st.reference(q, ot, ol))
+
+        def holes(tables, lens):
+            for j in sorted({1, k // 2, k - 1}):
+                tables[:, j] = -1
+            return tables, lens
+
+        got, ot, ol = st.decode(st.seqs, st.oseqs, q, shared=k, edit=holes)
+        ref = _reference_skipping(st, q, ot, ol)
+        st.check(got, ref)
+        # the ordinary decode reads the same entries the same way
+        plain, _, _ = st.decode(st.seqs, st.oseqs, q, edit=holes)
+        st.check(plain, ref)
     finally:
         st.close()
 
