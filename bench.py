@@ -70,13 +70,13 @@ WORKLOAD_NAMES = {
 # kernel source it was measured on (kernels_sha()); for any other source the
 # figure is not reported.
 MEASURED_TRAFFIC = {
-    "c3": (510.7e6, "82bbb07e146d99d1"),
-    "c2": (1985.6e6, "82bbb07e146d99d1"),
-    "c2_bs128": (2047.8e6, "82bbb07e146d99d1"),
-    "c5": (2154.2e6, "82bbb07e146d99d1"),
-    "c5_fp8": (1080.5e6, "82bbb07e146d99d1"),
-    "c5w": (72.1e6, "82bbb07e146d99d1"),
-    "c4": (390.3e6, "82bbb07e146d99d1"),   # the whole call: prefix, suffix and merge kernels
+    "c3": (510.8e6, "ec3761fdcaa40588"),
+    "c2": (1985.4e6, "ec3761fdcaa40588"),
+    "c2_bs128": (2047.8e6, "ec3761fdcaa40588"),
+    "c5": (2154.3e6, "ec3761fdcaa40588"),
+    "c5_fp8": (1080.5e6, "ec3761fdcaa40588"),
+    "c5w": (72.1e6, "ec3761fdcaa40588"),
+    "c4": (390.3e6, "ec3761fdcaa40588"),   # the whole call: prefix, suffix and merge kernels
 }
 
 
