@@ -613,6 +613,11 @@ template <int UB>
 __device__ __forceinline__ void table_entries_scalar(const int32_t* row, int32_t rel, int32_t n,
                                                      int32_t (&ids)[UB]) {
   static_assert(UB == 1 || UB == 2 || UB == 4, "blocks per unit");
+  if (n <= 0) {
+#pragma unroll
+    for (int k = 0; k < UB; ++k) ids[k] = -1;
+    return;
+  }
   uint32_t off[UB];
 #pragma unroll
   for (int k = 0; k < UB; ++k) off[k] = 4u * (uint32_t)(rel + k < n ? rel + k : n - 1);
@@ -633,6 +638,14 @@ __device__ __forceinline__ void table_entries_scalar(const int32_t* row, int32_t
   }
 #pragma unroll
   for (int k = 0; k < UB; ++k) ids[k] = rel + k < n ? ids[k] : -1;
+}
+
+// One wave-uniform int32 read with a scalar load (counted by lgkmcnt, not
+// with the vector loads in flight).
+__device__ __forceinline__ int32_t scalar_load_i32(const int32_t* p) {
+  int32_t v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
 }
 
 // LDS slots of the shared-prefix pipeline (16 KiB each); two workgroups of
@@ -1002,7 +1015,19 @@ struct Decoder {
                                                  int b) {
     Seg s;
     int32_t nu;
-    const int32_t raw = C && P.lens_in_lds ? C[P.batch + 1 + b] : P.lens[b];
+    int32_t raw;
+    if constexpr (KV != KV_FP8) {
+      // Two loads of their own, each made uniform in its branch: written as
+      // one select, they become a single generic (flat) load, which counts
+      // as a vector load too, and waiting for it waits for every K/V load
+      // in flight.
+      if (C && P.lens_in_lds)
+        raw = uniform(((const __attribute__((address_space(3))) int32_t*)C)[P.batch + 1 + b]);
+      else
+        raw = scalar_load_i32(P.lens + b);
+    } else {
+      raw = C && P.lens_in_lds ? C[P.batch + 1 + b] : P.lens[b];
+    }
     extent_of<BS, U>(P, raw, &s.L, &s.lo, &s.first, &nu);
     s.g = g;
     s.b = b;
@@ -1436,9 +1461,9 @@ struct Decoder {
   // One wavefront's units [r0, r1) (KV-head-major global unit indices; the
   // first lies in pair (g0, b0)) as one stream of sub-tiles: the loads run
   // one sub-tile ahead of the math across piece boundaries, and the next
-  // piece's block-table entries and queries are fetched while the current
-  // piece streams.  C: unit prefix sums (NULL in single mode, where the range
-  // is the whole of one pair).
+  // piece's queries (FP8: also its first block-table entries) are fetched
+  // while the current piece streams.  C: unit prefix sums (NULL in single
+  // mode, where the range is the whole of one pair).
   static __device__ void stream(const DecodeParams& P, const int32_t* C, int64_t t_head, int64_t T, int64_t W,
                                 int64_t w, int64_t r0, int64_t r1, int g0, int b0, uint8_t* stage) {
     const int lane = threadIdx.x & 63;
@@ -1452,8 +1477,18 @@ struct Decoder {
     int64_t lend = min(r1, ls.start + ls.nb);
     int32_t tb0, tb1;
     piece_blocks(ls, lbeg, lend, &tb0, &tb1);
-    int32_t tcur = table_chunk(P, ls.b, tb0, tb1, 0, lane);
-    int32_t tnext = tb1 - tb0 > 64 ? table_chunk(P, ls.b, tb0, tb1, 1, lane) : -1;
+    // Block-table entries: FP8 reads them 64 at a time, one per lane (the
+    // next 64 and the next piece's first 64 prefetched); the other types read
+    // each sub-tile's entries with scalar loads.  A vector load of entries
+    // for a later sub-tile needs a register copy where the code paths join,
+    // and the copy waits for every load in flight; scalar loads are counted
+    // apart from the vector loads.
+    constexpr bool SCALAR_TABLE = KV != KV_FP8;
+    int32_t tcur = -1, tnext = -1;
+    if constexpr (!SCALAR_TABLE) {
+      tcur = table_chunk(P, ls.b, tb0, tb1, 0, lane);
+      tnext = tb1 - tb0 > 64 ? table_chunk(P, ls.b, tb0, tb1, 1, lane) : -1;
+    }
     int ccur = 0;
     // the piece after it, with its first table entries in flight (looked up
     // once the first sub-tile's loads are out)
@@ -1476,27 +1511,35 @@ struct Decoder {
         lbeg = lend;
         lend = min(r1, ls.start + ls.nb);
         piece_blocks(ls, lbeg, lend, &tb0, &tb1);
-        tcur = tpn;
-        tnext = tb1 - tb0 > 64 ? table_chunk(P, ls.b, tb0, tb1, 1, lane) : -1;
-        ccur = 0;
+        if constexpr (!SCALAR_TABLE) {
+          tcur = tpn;
+          tnext = tb1 - tb0 > 64 ? table_chunk(P, ls.b, tb0, tb1, 1, lane) : -1;
+          ccur = 0;
+        }
         load_q(P, ls.b, ls.g, i, kg, qn);
         has_ln = lend < r1 && next_seg(P, C, t_head, ls, ln);
-        if (has_ln) {
-          int32_t nb0, nb1;
-          piece_blocks(ln, ln.start, min(r1, ln.start + ln.nb), &nb0, &nb1);
-          tpn = table_chunk(P, ln.b, nb0, nb1, 0, lane);
+        if constexpr (!SCALAR_TABLE) {
+          if (has_ln) {
+            int32_t nb0, nb1;
+            piece_blocks(ln, ln.start, min(r1, ln.start + ln.nb), &nb0, &nb1);
+            tpn = table_chunk(P, ln.b, nb0, nb1, 0, lane);
+          }
         }
       }
       const int rel = (int)(lx - lbeg) * UB;
-      const int c = rel >> 6;
-      if (c != ccur) {
-        tcur = tnext;
-        tnext = tb0 + 64 * (c + 1) < tb1 ? table_chunk(P, ls.b, tb0, tb1, c + 1, lane) : -1;
-        ccur = c;
-      }
       int32_t ids[UB];
+      if constexpr (SCALAR_TABLE) {
+        table_entries_scalar<UB>(P.tables + (int64_t)ls.b * P.max_blocks + tb0, rel, tb1 - tb0, ids);
+      } else {
+        const int c = rel >> 6;
+        if (c != ccur) {
+          tcur = tnext;
+          tnext = tb0 + 64 * (c + 1) < tb1 ? table_chunk(P, ls.b, tb0, tb1, c + 1, lane) : -1;
+          ccur = c;
+        }
 #pragma unroll
-      for (int k = 0; k < UB; ++k) ids[k] = __builtin_amdgcn_readlane(tcur, (rel & 63) + k);
+        for (int k = 0; k < UB; ++k) ids[k] = __builtin_amdgcn_readlane(tcur, (rel & 63) + k);
+      }
       const Addr a = locate(P, ls.g, ids, lsub, (tb0 + rel) * BS + lsub * TT, i, kg);
       last = lsub == SPU - 1 && lx + 1 == lend;
       if (++lsub == SPU) {
@@ -1547,10 +1590,12 @@ struct Decoder {
     load_v(V0, a0);
     __builtin_amdgcn_sched_barrier(0);
     has_ln = C && lend < r1 && next_seg(P, C, t_head, ls, ln);
-    if (has_ln) {
-      int32_t nb0, nb1;
-      piece_blocks(ln, ln.start, min(r1, ln.start + ln.nb), &nb0, &nb1);
-      tpn = table_chunk(P, ln.b, nb0, nb1, 0, lane);
+    if constexpr (!SCALAR_TABLE) {
+      if (has_ln) {
+        int32_t nb0, nb1;
+        piece_blocks(ln, ln.start, min(r1, ln.start + ln.nb), &nb0, &nb1);
+        tpn = table_chunk(P, ln.b, nb0, nb1, 0, lane);
+      }
     }
     // sched_barrier keeps the compiler from hoisting the next sub-tile's
     // loads above the current one's math (that would hold three half-tiles
