@@ -1941,7 +1941,7 @@ __device__ __forceinline__ void load_row(const uint8_t* p, int64_t row, int lane
 // code slowed its stream loop.
 template <int D, int NKV, int NSRC>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeParams P, TailParams TP) {
-  constexpr int NPC = 8;   // pieces per thread per batch
+  constexpr int NPC = 4;   // pieces per thread per batch
   constexpr bool FUSED = NKV >= 0;
   constexpr int KV = FUSED ? NKV : KV_F32;
   constexpr int SRC = FUSED ? NSRC : KV_F32;
