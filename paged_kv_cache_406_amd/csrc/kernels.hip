@@ -1212,8 +1212,12 @@ struct Decoder {
     *end = uniform(t->end);
   }
 
-  // Query-row tiles (MFMA column blocks of 16 rows) per wavefront of prefix_kernel.
-  static constexpr int NT = 2;
+  // Query-row tiles (MFMA column blocks of 16 rows) per wavefront of
+  // prefix_kernel.  With one tile a wavefront needs at most 168 registers
+  // (three per SIMD), so three workgroups share a CU; per query row the work
+  // is the same as with two tiles, and the grid then needs fewer token
+  // chunks.
+  static constexpr int NT = 1;
   // 16-byte K and V groups of one sub-tile: one per lane per load of load_k /
   // load_v, so a wavefront's loads of a sub-tile are exactly the sub-tile.
   static constexpr int KG = NKL * 64;
@@ -1235,7 +1239,10 @@ struct Decoder {
   // Online softmax of one row tile of the shared prefix (the decode's
   // softmax with the masking decided per sub-tile by the caller): with MASK,
   // tokens at or past the row's L, or in a block that is not real, get
-  // probability 0.
+  // probability 0.  scale_log2 >= 0 (the caller flips the sign of the
+  // queries for a negative scale), so the row maximum of the scaled scores
+  // is the scaled maximum of the raw ones, and each exponent is one fused
+  // multiply-add.  Without MASK every score is finite.
   template <bool MASK>
   static __device__ __forceinline__ void prefix_softmax(const VTile& T, const f32x4 (&S)[NQT], State& st,
                                                         float (&p)[NQT][4], int32_t L, float scale_log2, int kg) {
@@ -1244,10 +1251,11 @@ struct Decoder {
     for (int t = 0; t < NQT; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        s[t][r] = S[t][r] * scale_log2;
         if constexpr (MASK) {
           const int32_t tok = T.tok0 + TPG * kg + 4 * t + r;
-          s[t][r] = T.ok && tok < L ? s[t][r] : -INFINITY;
+          s[t][r] = T.ok && tok < L ? S[t][r] * scale_log2 : -INFINITY;
+        } else {
+          s[t][r] = S[t][r];
         }
       }
     float bmax = s[0][0];
@@ -1256,6 +1264,7 @@ struct Decoder {
 #pragma unroll
       for (int r = 0; r < 4; ++r) bmax = fmaxf(bmax, s[t][r]);
     bmax = row_max4(bmax);
+    if constexpr (!MASK) bmax *= scale_log2;
     const bool up = bmax > st.m + RESCALE_LOG2;   // the first finite score always moves it
     if (__any(up)) {
       const float alpha = up ? __builtin_amdgcn_exp2f(st.m - bmax) : 1.0f;
@@ -1270,10 +1279,62 @@ struct Decoder {
     for (int t = 0; t < NQT; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        p[t][r] = __builtin_amdgcn_exp2f(s[t][r] - m_use);
+        if constexpr (MASK) {
+          p[t][r] = __builtin_amdgcn_exp2f(s[t][r] - m_use);
+        } else {
+          p[t][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], scale_log2, -m_use));
+        }
         psum += p[t][r];
       }
     st.l += psum;
+  }
+
+  // P = hi + lo for the P.V products of the shared prefix (16-bit-float
+  // MFMA operands of bf16 and FP8 pools): hi = p rounded to bf16, lo = the
+  // rest p - hi rounded to bf16, as the decode's P.V takes it; two values per
+  // conversion, hi widened back with a shift and a mask.
+  static __device__ __forceinline__ void split_p(const float (&p)[NQT][4], bf16x8 (&hi)[TPG / 8],
+                                                 bf16x8 (&lo)[TPG / 8]) {
+#pragma unroll
+    for (int c = 0; c < TPG / 8; ++c) {
+      u32x4 hw, lw;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int e = 8 * c + 2 * k;
+        const float a = p[e / 4][e % 4], b = p[(e + 1) / 4][(e + 1) % 4];
+        const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+        const f32x2 r = {a - __uint_as_float(h << 16), b - __uint_as_float(h & 0xffff0000u)};
+        hw[k] = h;
+        lw[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
+      }
+      hi[c] = __builtin_bit_cast(bf16x8, hw);
+      lo[c] = __builtin_bit_cast(bf16x8, lw);
+    }
+  }
+
+  // O += P.V of the shared prefix, V already masked.
+  static __device__ __forceinline__ void prefix_pv(const VTile& T, const float (&p)[NQT][4], State& st) {
+    if constexpr (KV == KV_F32 || KV == KV_F16) {
+      pv_acc(T, p, st);
+    } else {
+      bf16x8 phi[TPG / 8], plo[TPG / 8];
+      split_p(p, phi, plo);
+#pragma unroll
+      for (int n = 0; n < NV; ++n) {
+        if constexpr (KV == KV_BF16) {
+          const bf16x8 a = as8<bf16x8>(T.v[n]);
+          st.O[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi[0], st.O[n], 0, 0, 0);
+          st.O[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo[0], st.O[n], 0, 0, 0);
+        } else {
+          const bf16x8 a0 = e4m3x8_to_bf16x8(T.v[n].x, T.v[n].y);
+          const bf16x8 a1 = e4m3x8_to_bf16x8(T.v[n].z, T.v[n].w);
+          st.O[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, phi[0], st.O[n], 0, 0, 0);
+          st.O[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, plo[0], st.O[n], 0, 0, 0);
+          st.O[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, phi[1], st.O[n], 0, 0, 0);
+          st.O[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, plo[1], st.O[n], 0, 0, 0);
+        }
+      }
+    }
   }
 
   // One staged sub-tile of the shared prefix for this wavefront's NT row
@@ -1292,7 +1353,7 @@ struct Decoder {
     }
     if constexpr (MASK) mask_v(V, V.tok0 + TPG * kg, 0, kT);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) pv_acc(V, pp[t], st[t]);
+    for (int t = 0; t < NT; ++t) prefix_pv(V, pp[t], st[t]);
   }
 
   // Shared prefix, one workgroup of 4 wavefronts: query rows
@@ -1326,6 +1387,16 @@ struct Decoder {
       const int hg = live[t] ? (int)(r % G) : 0;
       hrow[t] = (int64_t)b * P.hq + (int64_t)g * G + hg;
       load_q_at(P, g, hrow[t] * D, kg, q[t]);
+      // a negative scale: flip the queries' signs (exact) and use |scale|
+      if (P.scale_log2 < 0.f) {
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+          if constexpr (KV == KV_F32)
+            q[t][j] = -q[t][j];
+          else
+            q[t][j] = __builtin_bit_cast(qop, __builtin_bit_cast(u32x4, q[t][j]) ^ 0x80008000u);
+        }
+      }
       int32_t L = P.lens[b];
       L = L < 0 ? 0 : (L > cap ? cap : L);
       Lc[t] = live[t] ? min(L, kT) : 0;
@@ -1399,6 +1470,7 @@ struct Decoder {
       }
     }
 
+    const float scale_abs = __builtin_fabsf(P.scale_log2);
     if (s0 < s1) {
       // STAGES LDS slots: STAGES - 1 sub-tiles in flight while one is used;
       // sub-tile x lives in slot (x - s0) % STAGES
@@ -1428,13 +1500,13 @@ struct Decoder {
         KTile K;
         VTile V;
         next(s, K, V);
-        prefix_step<false>(K, V, q, st, Lc, kT, P.scale_log2, kg);
+        prefix_step<false>(K, V, q, st, Lc, kT, scale_abs, kg);
       }
       for (int32_t s = s_mid; s < s1; ++s) {
         KTile K;
         VTile V;
         next(s, K, V);
-        prefix_step<true>(K, V, q, st, Lc, kT, P.scale_log2, kg);
+        prefix_step<true>(K, V, q, st, Lc, kT, scale_abs, kg);
       }
     }
 
@@ -1873,7 +1945,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // KV-head major, so the workgroups of one head sit on one XCD and its prefix
 // blocks stay in that XCD's L2.
 template <int KV, int D, int BS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefix_kernel(DecodeParams P) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void prefix_kernel(DecodeParams P) {
   typedef Decoder<KV, D, BS> Dec;
   __shared__ __attribute__((aligned(16))) uint8_t stage[Dec::STAGES * Dec::STAGE_BYTES];
   int64_t wg = blockIdx.x;
@@ -2315,9 +2387,9 @@ static int tokens_per_subtile(int kv) {
   return kv == PKV_F32 ? SubTile<KV_F32>::TT : (kv == PKV_FP8_E4M3 ? SubTile<KV_FP8>::TT : SubTile<KV_BF16>::TT);
 }
 
-// Shared prefix work split: row groups (128 query rows, one workgroup) per
-// KV head and token chunks, about one workgroup per CU in all, at most 16
-// chunks.
+// Shared prefix work split: row groups (64 * NT query rows, one workgroup)
+// per KV head and token chunks, about three workgroups per CU in all, at
+// most 16 chunks.
 static void prefix_plan(const kv_pool* pool, const paged_decode_args* a, int cus, int32_t* rtiles,
                         int32_t* chunks) {
   const kv_pool_desc& d = pool->desc;
@@ -2326,8 +2398,9 @@ static void prefix_plan(const kv_pool* pool, const paged_decode_args* a, int cus
   const int64_t rt = ((int64_t)a->batch * G + rows_per_group - 1) / rows_per_group;
   const int64_t tt = tokens_per_subtile(d.kv_dtype);
   const int64_t nsp = ((int64_t)a->shared_prefix_blocks * d.block_size + tt - 1) / tt;
-  // two workgroups per CU (two wavefronts per SIMD hide each other's waits)
-  int64_t c = 2 * (int64_t)cus / std::max<int64_t>(1, d.num_kv_heads * rt);
+  // three workgroups per CU: three wavefronts per SIMD (at most 168
+  // registers each) hide each other's waits
+  int64_t c = 3 * (int64_t)cus / std::max<int64_t>(1, d.num_kv_heads * rt);
   c = std::max<int64_t>(1, std::min<int64_t>({c, nsp, 16}));
   *rtiles = (int32_t)rt;
   *chunks = (int32_t)c;

@@ -124,9 +124,10 @@ class FullState:
             list(ex.map(lambda t: self.opool.append(0, t[0], t[1], src, t[2]), self._pending))
         self._pending = []
 
-    def decode(self, seqs, oseqs, q, shared=0, splits=0, edit=None):
+    def decode(self, seqs, oseqs, q, shared=0, splits=0, edit=None, scale=None):
         """edit(tables, lens) -> (tables, lens), if given, changes the exported
-        tables and lengths (both sides' copies) before the call."""
+        tables and lengths (both sides' copies) before the call.  scale
+        defaults to 1/sqrt(D)."""
         w = self.w
         mb = max(len(self.bm.table(o)) for o in oseqs)
         tables, lens = P.block_table_export(self.pool.handle, seqs, mb)
@@ -138,7 +139,8 @@ class FullState:
         B = len(seqs)
         out = torch.full((B, w.num_q_heads, w.head_dim), float("nan"), dtype=torch.float32, device="cuda")
         qd, td, ld = to_dev(q), torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda()
-        a = P.make_decode_args(0, B, w.num_q_heads, mb, qd, w.q_dtype, td, ld, 1.0 / math.sqrt(w.head_dim), out,
+        scale = 1.0 / math.sqrt(w.head_dim) if scale is None else scale
+        a = P.make_decode_args(0, B, w.num_q_heads, mb, qd, w.q_dtype, td, ld, scale, out,
                                "f32", sliding_window=w.window, num_splits=splits, shared_prefix_blocks=shared)
         nbytes = P.paged_attention_workspace_size(self.pool.handle, a)
         ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
@@ -147,13 +149,13 @@ class FullState:
         torch.cuda.synchronize()
         return out_to_f64(out, "f32"), otables, olens
 
-    def reference(self, q, otables, olens):
+    def reference(self, q, otables, olens, scale=None):
         """The oracle's output of every row, rows split over the thread pool."""
         w = self.w
         B = len(olens)
         step = max(1, -(-B // (2 * THREADS)))
         parts = [np.arange(a, min(B, a + step)) for a in range(0, B, step)]
-        scale = 1.0 / math.sqrt(w.head_dim)
+        scale = 1.0 / math.sqrt(w.head_dim) if scale is None else scale
         with ThreadPoolExecutor(THREADS) as ex:
             outs = list(ex.map(lambda r: decode_attention(self.opool, 0, q[r], w.q_dtype, otables[r], olens[r],
                                                           scale, w.window), parts))

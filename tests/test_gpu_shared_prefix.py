@@ -67,6 +67,24 @@ def test_shared_prefix_decode_parity(name):
         st.close()
 
 
+@pytest.mark.parametrize("scale_mult", [-1.0, 0.0])
+@pytest.mark.parametrize("name", ["bf16_g4", "f16_mha", "fp8_g8", "f32_d64"])
+def test_shared_prefix_negative_and_zero_scale(name, scale_mult):
+    """The prefix pass works with the scale's magnitude and moves its sign
+    into the queries; a negative scale (softmax of the negated scores) and a
+    zero one (uniform weights) still give the oracle's attention."""
+    w, d, st = _family(name)
+    try:
+        k = P.block_table_common_prefix(st.pool.handle, st.seqs)
+        assert k > 0
+        q = wl.q_bits(w)
+        scale = scale_mult / math.sqrt(w.head_dim)
+        got, ot, ol = st.decode(st.seqs, st.oseqs, q, shared=k, scale=scale)
+        st.check(got, st.reference(q, ot, ol, scale=scale))
+    finally:
+        st.close()
+
+
 def _reference_skipping(st, q, tables, lens):
     """The decode's result when table entries outside the pool are empty
     blocks whose tokens are skipped (the decode's documented reading of such
