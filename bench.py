@@ -70,13 +70,13 @@ WORKLOAD_NAMES = {
 # kernel source it was measured on (kernels_sha()); for any other source the
 # figure is not reported.
 MEASURED_TRAFFIC = {
-    "c3": (511.1e6, "4983473d49d8dc95"),
-    "c2": (1985.7e6, "4983473d49d8dc95"),
-    "c2_bs128": (2047.5e6, "4983473d49d8dc95"),
-    "c5": (2155.3e6, "4983473d49d8dc95"),
-    "c5_fp8": (1080.5e6, "4983473d49d8dc95"),
-    "c5w": (72.2e6, "4983473d49d8dc95"),
-    "c4": (390.4e6, "4983473d49d8dc95"),   # the whole call: prefix, suffix and merge kernels
+    "c3": (511.1e6, "b5a2c31d033b0adb"),
+    "c2": (1985.7e6, "b5a2c31d033b0adb"),
+    "c2_bs128": (2047.6e6, "b5a2c31d033b0adb"),
+    "c5": (2155.4e6, "b5a2c31d033b0adb"),
+    "c5_fp8": (1080.5e6, "b5a2c31d033b0adb"),
+    "c5w": (72.3e6, "b5a2c31d033b0adb"),
+    "c4": (373.1e6, "b5a2c31d033b0adb"),   # the whole call: prefix, suffix and merge kernels
 }
 
 
