@@ -1988,12 +1988,13 @@ __device__ __forceinline__ void load_row(const uint8_t* p, int64_t row, int lane
 }
 
 // Log-sum-exp merge of the pieces of a split (KV head, sequence).  Merge
-// workgroup x < segs * pg is (seg, y) = (x / pg, x % pg); it owns a contiguous share
-// of the G * D/4 output positions (head h, 4 dims) of sequence-head seg; TPP
+// workgroup x < segs * pg is (seg, y) = (x / pg, x % pg) (with pg = 1, x
+// first spread over the XCDs, below); it owns a contiguous share of the
+// G * D/4 output positions (head h, 4 dims) of sequence-head seg; TPP
 // threads share a position, thread sub taking pieces sub, sub + TPP, ...
-// Each thread loads the (max, sum) and o of up to 8 of its pieces at once,
+// Each thread loads the (max, sum) and o of up to NPC of its pieces at once,
 // so the partials are read in one round trip after the job; more pieces are
-// folded in batches of 8 with the usual rescaling.  The thread maxima are
+// folded in batches of NPC with the usual rescaling.  The thread maxima are
 // combined by lane exchanges, then the rescaled sums by a butterfly that
 // leaves the same bits in every lane of a position (deterministic).  Piece p
 // of a job whose first piece is in range w0 is in slot (w0, first) for p = 0
@@ -2023,14 +2024,27 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams P, TailParams T
   // pool also store the new tokens
   int64_t nmeta = 0;
   if constexpr (FUSED) {
-    nmeta = merge_row_groups(P);
+    // their count padded to a multiple of 8, so that the merge workgroups
+    // after them start on XCD 0
+    const int64_t nreal = merge_row_groups(P);
+    nmeta = (nreal + 7) / 8 * 8;
     if ((int64_t)blockIdx.x < nmeta) {
-      if constexpr (KV == KV_FP8) append_group<D, KV, SRC, true>(P, TP, (int)blockIdx.x);
-      else update_rows(P, TP, (int)blockIdx.x);
+      if ((int64_t)blockIdx.x < nreal) {
+        if constexpr (KV == KV_FP8) append_group<D, KV, SRC, true>(P, TP, (int)blockIdx.x);
+        else update_rows(P, TP, (int)blockIdx.x);
+      }
       return;
     }
   }
-  const int64_t x = blockIdx.x - nmeta;
+  // With one workgroup per sequence-head and a multiple of 8 of them, the
+  // workgroups on one XCD take a contiguous eighth of the sequence-heads
+  // (KV-head major), the ones whose pieces the decode's wavefront ranges on
+  // that XCD wrote: the partials are read back on the XCD that wrote them.
+  int64_t x = blockIdx.x - nmeta;
+  {
+    const int64_t segs = (int64_t)P.batch * P.hkv;
+    if (P.merge_pg == 1 && segs % 8 == 0) x = (x % 8) * (segs / 8) + x / 8;
+  }
   const int64_t seg = x / P.merge_pg;
   const int yb = (int)(x % P.merge_pg);
   const int b = (int)(seg % P.batch), g = (int)(seg / P.batch);
@@ -2898,7 +2912,7 @@ static pkv_status decode_launch(const kv_pool* pool, const paged_decode_args* a,
     // the fused append's merge: every pair's own partial and the new token,
     // and the workgroups that write the rows' tables and lengths
     P.merge_pg = 1;
-    const int64_t mgrid = segs + merge_row_groups(P);
+    const int64_t mgrid = segs + (merge_row_groups(P) + 7) / 8 * 8;
     e = launch(mfn, dim3((uint32_t)mgrid), 0, s, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, P, TP);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
     if (nk) *nk = 2;
@@ -2932,7 +2946,7 @@ static pkv_status decode_launch(const kv_pool* pool, const paged_decode_args* a,
   int pg = 1;
   while (segs * pg < 512 && np / (pg * 2) >= 16) pg *= 2;
   P.merge_pg = pg;
-  const int64_t mgrid = segs * pg + (P.fused ? merge_row_groups(P) : 0);
+  const int64_t mgrid = segs * pg + (P.fused ? (merge_row_groups(P) + 7) / 8 * 8 : 0);
   e = launch(mfn, dim3((uint32_t)mgrid), 0, s, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, P, TP);
   if (e != hipSuccess) return hip_fail(e, "merge launch");
   if (nk) *nk = 2;
