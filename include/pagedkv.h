@@ -382,7 +382,11 @@ typedef struct {
    * L / block_size not below max_blocks_per_seq, leaves the row's table
    * entry and length as they were.  The slots are read on the device while
    * the call runs.
-   * Same result as paged_kv_append followed by paged_attention_decode. */
+   * Same result as paged_kv_append followed by paged_attention_decode.
+   * The tables and lengths belong to the step, not to a layer: in a pool of
+   * several layers, fuse the append into one call per step (the first
+   * layer's), and let every later layer store its own token with
+   * paged_kv_append and decode the L + 1 tokens. */
   const void* new_k;            /* device [B][Hkv][head_dim], 16-byte aligned */
   const void* new_v;            /* device [B][Hkv][head_dim], 16-byte aligned */
   int32_t new_dtype;            /* the pool's dtype, or f32 / f16 / bf16 into an FP8 pool */

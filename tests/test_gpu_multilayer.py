@@ -186,3 +186,94 @@ def test_decode_every_layer(name, splits):
         assert np.isfinite(got).all()
         err = np.abs(got - ref).max()
         assert err <= TOL[w.kv_dtype], (name, layer, splits, err)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_shared_prefix_every_layer(name):
+    """The longest sequence and its branch share their full leading blocks;
+    the shared-prefix decode (those blocks read once for both rows) of every
+    layer matches the oracle: the prefix pass's block addresses and FP8
+    scales are those of the layer asked for."""
+    st = _state(name)
+    w = st.w
+    h = st.pool.handle
+    b = int(np.argmax(st.d.lengths))
+    pair = [st.seqs[b], st.children[b]]
+    mb = max(len(st.bm.table(s)) for s in pair)
+    tables, lens = P.block_table_export(h, pair, mb)
+    ot, ol = st.bm.export(pair, mb)
+    assert np.array_equal(tables, ot) and np.array_equal(lens, ol)
+    k = P.block_table_common_prefix(h, pair)
+    assert k == st.bm.common_prefix(pair) and k >= 1
+    scale = 1.0 / math.sqrt(w.head_dim)
+    for layer in range(w.num_layers):
+        q = wl.q_bits(w, batch=2, stream=(7, layer))
+        ref = decode_attention(st.opool, layer, q, w.q_dtype, ot, ol, scale)
+        out = torch.full((2, w.num_q_heads, w.head_dim), float("nan"), dtype=torch.float32, device="cuda")
+        td = torch.from_numpy(np.ascontiguousarray(tables, dtype=np.int32)).cuda()
+        ld = torch.from_numpy(np.ascontiguousarray(lens, dtype=np.int32)).cuda()
+        qd = to_dev(q)
+        a = P.make_decode_args(layer, 2, w.num_q_heads, mb, qd, w.q_dtype, td, ld, scale, out, "f32",
+                               shared_prefix_blocks=k)
+        nbytes = P.paged_attention_workspace_size(h, a)
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+        a.workspace, a.workspace_bytes = ws.data_ptr(), nbytes
+        P.paged_attention_decode(h, a)
+        torch.cuda.synchronize()
+        got = out_to_f64(out, "f32")
+        assert np.isfinite(got).all()
+        err = np.abs(got - ref).max()
+        assert err <= TOL[w.kv_dtype], (name, layer, k, err)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_fused_step_in_first_layer(name):
+    """One decode step of a model of several layers over device-resident
+    tables and lengths.  Layer 0's call fuses the append: it stores layer 0's
+    token and writes each row's table entry and length, once for the step.
+    Every later layer stores its own token with paged_kv_append and decodes
+    the L + 1 tokens.  Every layer's output matches the oracle's append then
+    decode, and the tables and lengths advance by one token, not one per
+    layer."""
+    w = CASES[name]
+    st = MultiLayerState(w)    # a fresh pool: the step changes it
+    try:
+        h = st.pool.handle
+        seqs = st.all_seqs()
+        B = len(seqs)
+        mb = max(len(st.bm.table(s)) for s in seqs) + 1
+        t0, l0 = P.block_table_export(h, seqs, mb)
+        d_tables, d_lens = torch.from_numpy(t0).cuda(), torch.from_numpy(l0).cuda()
+        slots, cows = P.block_table_append_batch(h, seqs)
+        oslots, ocows = st.bm.append_batch(seqs)
+        assert slots.tolist() == oslots
+        assert len(cows) == 0 and len(ocows) == 0   # every row's last block is its own
+        d_slots = torch.from_numpy(np.asarray(slots, dtype=np.int64)).cuda()
+        ot, ol = st.bm.export(seqs, mb)
+        scale = 1.0 / math.sqrt(w.head_dim)
+        for layer in range(w.num_layers):
+            kb, vb = wl.kv_tokens_bits(w, (8, layer), B)
+            q = wl.q_bits(w, batch=B, stream=(9, layer))
+            kw = {}
+            if layer == 0:
+                kw = dict(new_k=to_dev(kb), new_v=to_dev(vb), new_dtype=w.src_dtype, new_slots=d_slots)
+            else:
+                P.paged_kv_append(h, layer, to_dev(kb), to_dev(vb), w.src_dtype, d_slots, B)
+            out = torch.full((B, w.num_q_heads, w.head_dim), float("nan"), dtype=torch.float32, device="cuda")
+            a = P.make_decode_args(layer, B, w.num_q_heads, mb, to_dev(q), w.q_dtype, d_tables, d_lens, scale, out,
+                                   "f32", **kw)
+            nbytes = P.paged_attention_workspace_size(h, a)
+            ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+            a.workspace, a.workspace_bytes = ws.data_ptr(), nbytes
+            P.paged_attention_decode(h, a)
+            torch.cuda.synchronize()
+            st.opool.append(layer, kb, vb, w.src_dtype, oslots)
+            ref = decode_attention(st.opool, layer, q, w.q_dtype, ot, ol, scale)
+            got = out_to_f64(out, "f32")
+            assert np.isfinite(got).all()
+            err = np.abs(got - ref).max()
+            assert err <= TOL[w.kv_dtype], (name, layer, err)
+            # one token further after layer 0's call, and no further after the others
+            assert np.array_equal(d_tables.cpu().numpy(), ot) and np.array_equal(d_lens.cpu().numpy(), ol), layer
+    finally:
+        st.close()
