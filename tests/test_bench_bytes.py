@@ -61,3 +61,17 @@ def test_fused_append_bytes():
     w8 = wl.WORKLOADS["c5_fp8"]
     assert wl.ELEM_BYTES[w8.kv_dtype] == 1
     assert bench.new_token_bytes(w8, 4) == 4 * 8 * 128 * 2 * (wl.ELEM_BYTES[w8.src_dtype] + 1)
+
+
+def test_more_than_one_gpu_is_refused():
+    """The bench measures one GPU: --gpus 2 (or a torchrun world of two) exits
+    with a message, before anything touches a device."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for argv, env in ((["--gpus", "2"], {}), ([], {"WORLD_SIZE": "2"})):
+        r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), *argv], capture_output=True, text=True,
+                           timeout=120, env={**os.environ, **env}, cwd=root)
+        assert r.returncode != 0
+        assert "one GPU" in r.stderr + r.stdout
