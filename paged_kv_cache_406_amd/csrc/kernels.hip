@@ -326,10 +326,22 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* kc, uint8_t* 
   const u32x4* s = reinterpret_cast<const u32x4*>(base + ((int64_t)layer * num_blocks + src) * tile_bytes);
   u32x4* d = reinterpret_cast<u32x4*>(base + ((int64_t)layer * num_blocks + dst) * tile_bytes);
   const int64_t n16 = tile_bytes / 16;
-  // streamed: neither copy is read again by this kernel, and dirty lines
-  // left in L2 would be written back while the next kernel runs
-  for (int64_t i = threadIdx.x; i < n16; i += blockDim.x)
-    __builtin_nontemporal_store(__builtin_nontemporal_load(s + i), d + i);
+  // Streamed: neither copy is read again by this kernel, and dirty lines
+  // left in L2 would be written back while the next kernel runs.  Each
+  // thread loads a batch of 16-byte groups before storing any of them: the
+  // source and destination blocks differ, but the compiler cannot know that
+  // and would otherwise wait for every load before the store after it.
+  constexpr int BATCH = 8;
+  const int64_t bd = blockDim.x;
+  int64_t i0 = threadIdx.x;
+  for (; i0 + (BATCH - 1) * bd < n16; i0 += BATCH * bd) {
+    u32x4 v[BATCH];
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) v[k] = __builtin_nontemporal_load(s + i0 + k * bd);
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) __builtin_nontemporal_store(v[k], d + i0 + k * bd);
+  }
+  for (; i0 < n16; i0 += bd) __builtin_nontemporal_store(__builtin_nontemporal_load(s + i0), d + i0);
 }
 
 // ---------------------------------------------------------------------------
