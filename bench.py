@@ -70,13 +70,13 @@ WORKLOAD_NAMES = {
 # kernel source it was measured on (kernels_sha()); for any other source the
 # figure is not reported.
 MEASURED_TRAFFIC = {
-    "c3": (511.1e6, "2f4eb0967c5f9578"),
-    "c2": (1985.7e6, "2f4eb0967c5f9578"),
-    "c2_bs128": (2047.3e6, "2f4eb0967c5f9578"),
-    "c5": (2155.4e6, "2f4eb0967c5f9578"),
-    "c5_fp8": (1080.5e6, "2f4eb0967c5f9578"),
-    "c5w": (72.1e6, "2f4eb0967c5f9578"),
-    "c4": (373.6e6, "2f4eb0967c5f9578"),   # the whole call: prefix, suffix and merge kernels
+    "c3": (511.0e6, "f2f9a337c66b7863"),
+    "c2": (1985.8e6, "f2f9a337c66b7863"),
+    "c2_bs128": (2047.5e6, "f2f9a337c66b7863"),
+    "c5": (2155.3e6, "f2f9a337c66b7863"),
+    "c5_fp8": (1080.5e6, "f2f9a337c66b7863"),
+    "c5w": (72.1e6, "f2f9a337c66b7863"),
+    "c4": (373.6e6, "f2f9a337c66b7863"),   # the whole call: prefix, suffix and merge kernels
 }
 
 
